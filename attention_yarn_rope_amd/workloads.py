@@ -1,0 +1,165 @@
+"""Seeded synthetic workloads: input tensors and work counts.
+
+This module draws random inputs and counts work; it holds none of the
+attention or RoPE arithmetic. The HIP path (via the binding) and the CPU oracle
+consume the very same CPU tensors it returns.
+
+Generation recipe (one torch.Generator per workload, seeded, in this order):
+  1. sequence lengths, if the workload has any: torch.randint(lo, hi + 1, (n,));
+  2. q, then k, then v: torch.randn(shape, dtype=float32) rounded to bfloat16;
+     for a decode KV cache, sequence by sequence, K rows then V rows of the
+     valid length only (rows past the length stay zero);
+  3. sinks: torch.randn(num_q_heads, dtype=float32).
+
+The shapes follow GPT-OSS's attention: 64 query heads and 8 KV heads of width
+64 (q_proj 2880->4096, k_proj / v_proj 2880->512 in the gpt-oss-20b module
+print-out), scale 64 ** -0.5.
+"""
+
+from dataclasses import dataclass, field
+
+import torch
+
+HQ, HKV, HEAD_DIM = 64, 8, 64
+SCALE = HEAD_DIM ** -0.5
+WINDOW = 128
+
+
+@dataclass
+class Prefill:
+    name: str
+    layout: str                      # "bshd" or "thd"
+    q: torch.Tensor                  # bshd [B,S,Hq,D] / thd [T,Hq,D], bf16, CPU
+    k: torch.Tensor
+    v: torch.Tensor
+    sinks: torch.Tensor              # fp32 [Hq]
+    cu_seqlens: torch.Tensor = None  # int32 [N+1] (thd only)
+    lengths: list = field(default_factory=list)
+
+    @property
+    def seq_lengths(self):
+        if self.layout == "thd":
+            return list(self.lengths)
+        return [self.q.shape[1]] * self.q.shape[0]
+
+    @property
+    def max_seqlen(self):
+        return max(self.seq_lengths) if self.seq_lengths else 0
+
+
+@dataclass
+class Decode:
+    name: str
+    q: torch.Tensor                  # [N,Hq,D] bf16, un-rotated
+    k_cache: torch.Tensor            # [N,Lmax,Hkv,D] bf16, K taken as already rotated
+    v_cache: torch.Tensor
+    cache_seqlens: torch.Tensor      # int32 [N], includes the new token
+    sinks: torch.Tensor
+    lengths: list = field(default_factory=list)
+
+
+def _randn_bf16(shape, g):
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def prefill_bshd(B, S, seed, hq=HQ, hkv=HKV, d=HEAD_DIM, name=None):
+    g = torch.Generator().manual_seed(seed)
+    q = _randn_bf16((B, S, hq, d), g)
+    k = _randn_bf16((B, S, hkv, d), g)
+    v = _randn_bf16((B, S, hkv, d), g)
+    sinks = torch.randn(hq, generator=g, dtype=torch.float32)
+    return Prefill(name or f"bshd_B{B}_S{S}", "bshd", q, k, v, sinks)
+
+
+def prefill_thd(num_seqs, lo, hi, seed, hq=HQ, hkv=HKV, d=HEAD_DIM, lengths=None, name=None):
+    """Packed sequences with lengths uniform in [lo, hi] (or the given lengths)."""
+    g = torch.Generator().manual_seed(seed)
+    if lengths is None:
+        lengths = torch.randint(lo, hi + 1, (num_seqs,), generator=g).tolist()
+    lengths = [int(x) for x in lengths]
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    T = cu[-1]
+    q = _randn_bf16((T, hq, d), g)
+    k = _randn_bf16((T, hkv, d), g)
+    v = _randn_bf16((T, hkv, d), g)
+    sinks = torch.randn(hq, generator=g, dtype=torch.float32)
+    return Prefill(name or f"thd_N{len(lengths)}_T{T}", "thd", q, k, v, sinks,
+                   cu_seqlens=torch.tensor(cu, dtype=torch.int32), lengths=lengths)
+
+
+def decode(num_seqs, lo, hi, seed, max_len=None, hq=HQ, hkv=HKV, d=HEAD_DIM, lengths=None, name=None):
+    """One query token per sequence, cache lengths uniform in [lo, hi] (incl. the new token)."""
+    g = torch.Generator().manual_seed(seed)
+    if lengths is None:
+        lengths = torch.randint(lo, hi + 1, (num_seqs,), generator=g).tolist()
+    lengths = [int(x) for x in lengths]
+    N = len(lengths)
+    Lmax = max_len if max_len is not None else hi
+    q = _randn_bf16((N, hq, d), g)
+    kc = torch.zeros((N, Lmax, hkv, d), dtype=torch.bfloat16)
+    vc = torch.zeros((N, Lmax, hkv, d), dtype=torch.bfloat16)
+    for n, L in enumerate(lengths):
+        kc[n, :L] = _randn_bf16((L, hkv, d), g)
+        vc[n, :L] = _randn_bf16((L, hkv, d), g)
+    sinks = torch.randn(hq, generator=g, dtype=torch.float32)
+    return Decode(name or f"decode_N{N}", q, kc, vc, torch.tensor(lengths, dtype=torch.int32), sinks,
+                  lengths=lengths)
+
+
+# The five workloads of this attention path: a tiny prefill, a dense 4K BSHD
+# prefill, packed THD sequences, a 128K-token prefill and a 64-sequence decode.
+def tiny(seed=0):
+    return prefill_bshd(1, 256, seed, name="tiny_B1_S256")
+
+
+def dense(seed=1):
+    return prefill_bshd(4, 4096, seed, name="dense_B4_S4096")
+
+
+def thd(seed=2):
+    return prefill_thd(16, 128, 8192, seed, name="thd_16seq")
+
+
+def long_context(seed=3):
+    return prefill_bshd(1, 131072, seed, name="long_B1_S131072")
+
+
+def decode64(seed=4):
+    return decode(64, 1024, 32768, seed, max_len=32768, name="decode_64seq")
+
+
+# ---- work counts (what the throughput figures divide by) ----
+
+def visible_pairs(length, window):
+    """Number of (query, key) position pairs with j <= i and (window == 0 or i - j < window)."""
+    n = int(length)
+    if window <= 0 or window >= n:
+        return n * (n + 1) // 2
+    w = int(window)
+    return w * (w + 1) // 2 + (n - w) * w
+
+
+def prefill_flops(lengths, window, hq=HQ, d=HEAD_DIM):
+    """Unmasked FLOPs: 2*D for q.k plus 2*D for p*v per visible pair and query head."""
+    return 4 * d * hq * sum(visible_pairs(n, window) for n in lengths)
+
+
+def prefill_bytes(total_tokens, table_rows, hq=HQ, hkv=HKV, d=HEAD_DIM, rotary_dim=HEAD_DIM):
+    """Read q, k, v once, write o once (bf16), read the sinks (fp32) and the bf16 table rows."""
+    return (total_tokens * (2 * hq * d * 2 + 2 * hkv * d * 2)
+            + hq * 4 + table_rows * rotary_dim * 2)
+
+
+def decode_bytes(lengths, window, hq=HQ, hkv=HKV, d=HEAD_DIM, rotary_dim=HEAD_DIM):
+    """Visible K/V rows + q in + o out + sinks + one table row and one length per sequence."""
+    kv_rows = sum(min(L, window) if window > 0 else L for L in lengths)
+    N = len(lengths)
+    return (kv_rows * hkv * d * 2 * 2 + N * hq * d * 2 * 2 + hq * 4
+            + N * rotary_dim * 2 + N * 4)
+
+
+def decode_flops(lengths, window, hq=HQ, d=HEAD_DIM):
+    kv_rows = sum(min(L, window) if window > 0 else L for L in lengths)
+    return 4 * d * hq * kv_rows
