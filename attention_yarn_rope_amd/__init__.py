@@ -1,0 +1,17 @@
+"""GPT-OSS attention hot path on MI355X: YaRN RoPE, sink + GQA + sliding-window
+prefill (BSHD and packed THD) and split-KV decode, as hand-written gfx950 HIP
+kernels behind a C ABI (include/gptoss_attn.h). This package is the thin torch
+binding; libgptoss_attn.so is loaded on first use and is required.
+"""
+
+from .api import (  # noqa: F401
+    rope_config,
+    yarn_params,
+    rope_table,
+    rope_qk,
+    attn_prefill,
+    attn_decode,
+    prefill_workspace_size,
+    decode_workspace_size,
+)
+from ._lib import GptossError, load as load_library  # noqa: F401

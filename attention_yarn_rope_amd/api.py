@@ -1,0 +1,159 @@
+"""Python binding of the C ABI: torch tensors in, torch tensors out.
+
+Argument marshalling only -- shapes and strides are read off the tensors, device
+memory comes from torch's allocator, work is enqueued on torch's current stream.
+Every step of the computation runs in the HIP kernels of libgptoss_attn.so.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import RopeConfig, SeqDesc, I64x2, I64x3, check
+
+HEAD_DIM = 64
+
+
+def rope_config(head_dim=64, rotary_dim=None, base=150000.0, scaling_factor=32.0,
+                initial_context_length=4096, ntk_alpha=1.0, ntk_beta=32.0):
+    """RoPE settings; defaults are GPT-OSS's (RotaryEmbedding on the rope_utils page)."""
+    return RopeConfig(head_dim, head_dim if rotary_dim is None else rotary_dim, float(base),
+                      float(scaling_factor), int(initial_context_length), float(ntk_alpha), float(ntk_beta))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA bfloat16 tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return t
+
+
+def _strides3(t, layout):
+    s = t.stride()
+    return I64x3(s[0], s[1], s[2]) if layout == _lib.BSHD else I64x3(0, s[0], s[1])
+
+
+def yarn_params(cfg=None):
+    """Host fp64 YaRN frequencies (rotary_dim/2 values) and concentration."""
+    cfg = cfg or rope_config()
+    n = cfg.rotary_dim // 2
+    om = (ctypes.c_double * n)()
+    c = ctypes.c_double()
+    check("gptoss_yarn_params", _lib.load().gptoss_yarn_params(ctypes.byref(cfg), om, ctypes.byref(c)))
+    return list(om), c.value
+
+
+def rope_table(num_positions, cfg=None, device="cuda"):
+    """bf16 [num_positions, rotary_dim] table: cos half then sin half, concentration applied."""
+    cfg = cfg or rope_config()
+    t = torch.empty((num_positions, cfg.rotary_dim), dtype=torch.bfloat16, device=device)
+    check("gptoss_rope_table_init",
+          _lib.load().gptoss_rope_table_init(ctypes.byref(cfg), num_positions, _ptr(t), _stream()))
+    return t
+
+
+def _desc(q, k, cu_seqlens, max_seqlen):
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("BSHD q must be [B, S, Hq, D]")
+        B, S, Hq, D = q.shape
+        return SeqDesc(_lib.BSHD, B, S, S, None, Hq, k.shape[2], D), _lib.BSHD
+    if q.dim() != 3:
+        raise ValueError("THD q must be [T, Hq, D]")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
+        raise TypeError("cu_seqlens must be a contiguous CUDA int32 tensor")
+    T, Hq, D = q.shape
+    if max_seqlen is None:
+        raise ValueError("THD needs max_seqlen (a host-side bound of the sequence lengths)")
+    return SeqDesc(_lib.THD, cu_seqlens.numel() - 1, T, int(max_seqlen), ctypes.c_void_p(cu_seqlens.data_ptr()),
+                   Hq, k.shape[1], D), _lib.THD
+
+
+def rope_qk(q, k, table, cu_seqlens=None, max_seqlen=None):
+    """Rotate q and k (BSHD [B,S,H,D] or THD [T,H,D] with cu_seqlens) into new contiguous tensors."""
+    _bf16(q, "q"), _bf16(k, "k"), _bf16(table, "table")
+    desc, layout = _desc(q, k, cu_seqlens, max_seqlen)
+    q_out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    k_out = torch.empty(k.shape, dtype=k.dtype, device=k.device)
+    check("gptoss_rope_qk", _lib.load().gptoss_rope_qk(
+        ctypes.byref(desc), _ptr(q), _strides3(q, layout), _ptr(k), _strides3(k, layout),
+        _ptr(q_out), _ptr(k_out), _ptr(table), table.shape[0], table.shape[1], _stream()))
+    return q_out, k_out
+
+
+def prefill_workspace_size(q, k, cu_seqlens=None, max_seqlen=None):
+    desc, _ = _desc(q, k, cu_seqlens, max_seqlen)
+    return _lib.load().gptoss_attn_prefill_workspace_size(ctypes.byref(desc))
+
+
+def attn_prefill(q, k, v, sinks, window=0, table=None, softmax_scale=None, cu_seqlens=None, max_seqlen=None,
+                 out=None, workspace=None, k_rotation="auto"):
+    """Sink + GQA + causal/sliding-window attention over BSHD or packed THD inputs.
+
+    With ``table`` q and k are rotated on the fly; without it they are taken as
+    already rotated. Returns ``out`` (bf16, q's shape).
+    """
+    _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v")
+    if sinks.dtype != torch.float32 or not sinks.is_cuda or not sinks.is_contiguous():
+        raise TypeError("sinks must be a contiguous CUDA float32 tensor")
+    desc, layout = _desc(q, k, cu_seqlens, max_seqlen)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _bf16(out, "out")
+    lib = _lib.load()
+    need = lib.gptoss_attn_prefill_workspace_size(ctypes.byref(desc))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    if table is not None:
+        _bf16(table, "table")
+    check("gptoss_attn_prefill_ex", lib.gptoss_attn_prefill_ex(
+        ctypes.byref(desc), _ptr(q), _strides3(q, layout), _ptr(k), _strides3(k, layout),
+        _ptr(v), _strides3(v, layout), _ptr(sinks), float(scale), int(window), tptr, trows, tdim,
+        _ptr(out), _strides3(out, layout), _ptr(workspace), workspace.numel(), _lib.KROT[k_rotation],
+        _stream()))
+    return out
+
+
+def decode_workspace_size(num_seqs, num_q_heads, max_cache_len, num_splits=0):
+    return _lib.load().gptoss_attn_decode_workspace_size(num_seqs, num_q_heads, max_cache_len, num_splits)
+
+
+def attn_decode(q, k_cache, v_cache, cache_seqlens, sinks, window=0, table=None, softmax_scale=None,
+                num_splits=0, out=None, workspace=None):
+    """One query token per sequence: q [N,Hq,D], caches [N,Lmax,Hkv,D], cache_seqlens int32 [N]."""
+    _bf16(q, "q"), _bf16(k_cache, "k_cache"), _bf16(v_cache, "v_cache")
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda:
+        raise TypeError("cache_seqlens must be a CUDA int32 tensor")
+    if sinks.dtype != torch.float32 or not sinks.is_cuda or not sinks.is_contiguous():
+        raise TypeError("sinks must be a contiguous CUDA float32 tensor")
+    N, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lib = _lib.load()
+    need = lib.gptoss_attn_decode_workspace_size(N, Hq, Lmax, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    ks = k_cache.stride()
+    check("gptoss_attn_decode", lib.gptoss_attn_decode(
+        N, Hq, Hkv, D, _ptr(q), I64x2(q.stride(0), q.stride(1)), _ptr(k_cache), _ptr(v_cache),
+        I64x3(ks[0], ks[1], ks[2]), _ptr(cache_seqlens), Lmax, _ptr(sinks), float(scale), int(window),
+        tptr, trows, tdim, _ptr(out), I64x2(out.stride(0), out.stride(1)), _ptr(workspace),
+        workspace.numel(), int(num_splits), _stream()))
+    return out

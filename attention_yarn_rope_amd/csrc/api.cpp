@@ -1,0 +1,416 @@
+// C ABI of the GPT-OSS attention library: argument checks, YaRN parameters on
+// the host, workspace sizing and kernel dispatch. Declared in gptoss_attn.h.
+#include "gptoss_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+using namespace gptoss;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gptoss_status fail(gptoss_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gptoss_status fail(gptoss_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gptoss_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return GPTOSS_OK;
+  return fail(GPTOSS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool strides_ok(const int64_t* s, int n) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0 || (s[i] & 7) != 0) return false;
+  return true;
+}
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// YaRN (page "nemo_automodel.components.models.gpt_oss.rope_utils",
+// RotaryEmbedding._compute_concentration_and_inv_freq): theta_i =
+// base^(-2i/d); with s > 1 the ramp gamma_i = clamp((i - lo) / (hi - lo), 0, 1)
+// between lo = (d/2) ln(L0 / (2 pi beta_fast)) / ln(base) and
+// hi = (d/2) ln(L0 / (2 pi beta_slow)) / ln(base) blends theta_i (gamma = 0)
+// into theta_i / s (gamma = 1); concentration 0.1 ln(s) + 1.
+gptoss_status yarn(const gptoss_rope_config* cfg, double* omega, double* conc) {
+  if (!cfg) return fail(GPTOSS_ERR_NULL, "rope config is NULL");
+  const int d = cfg->rotary_dim;
+  if (d <= 0 || (d & 1) || d > cfg->head_dim || d / 2 > kMaxPairs)
+    return fail(GPTOSS_ERR_SHAPE, "rotary_dim %d must be even, in (0, head_dim=%d] and <= %d", d,
+                cfg->head_dim, 2 * kMaxPairs);
+  if (!(cfg->base > 1.0) || !std::isfinite(cfg->base))
+    return fail(GPTOSS_ERR_SHAPE, "RoPE base must be finite and > 1");
+  const int half = d / 2;
+  const double s = cfg->scaling_factor;
+  double c = 1.0;
+  if (s > 1.0) {
+    if (!(cfg->initial_context_length > 0) || !(cfg->ntk_alpha > 0.0) || !(cfg->ntk_beta > cfg->ntk_alpha))
+      return fail(GPTOSS_ERR_SHAPE, "YaRN needs initial_context_length > 0 and 0 < ntk_alpha < ntk_beta");
+    const double L0 = (double)cfg->initial_context_length;
+    const double lb = std::log(cfg->base);
+    const double lo = half * std::log(L0 / (2.0 * M_PI * cfg->ntk_beta)) / lb;
+    const double hi = half * std::log(L0 / (2.0 * M_PI * cfg->ntk_alpha)) / lb;
+    for (int i = 0; i < half; ++i) {
+      const double theta = std::pow(cfg->base, -(2.0 * i) / d);
+      double gam = (i - lo) / (hi - lo);
+      gam = gam < 0.0 ? 0.0 : (gam > 1.0 ? 1.0 : gam);
+      omega[i] = theta * (1.0 - gam) + (theta / s) * gam;
+    }
+    c = 0.1 * std::log(s) + 1.0;
+  } else {
+    for (int i = 0; i < half; ++i) omega[i] = std::pow(cfg->base, -(2.0 * i) / d);
+  }
+  *conc = c;
+  return GPTOSS_OK;
+}
+
+gptoss_status check_desc(const gptoss_seq_desc* d) {
+  if (!d) return fail(GPTOSS_ERR_NULL, "sequence descriptor is NULL");
+  if (d->layout != GPTOSS_BSHD && d->layout != GPTOSS_THD)
+    return fail(GPTOSS_ERR_SHAPE, "layout %d is neither BSHD (0) nor THD (1)", d->layout);
+  if (d->batch < 0 || d->seqlen < 0) return fail(GPTOSS_ERR_SHAPE, "negative batch or seqlen");
+  if (d->head_dim != kHeadDim)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", d->head_dim);
+  if (d->num_kv_heads < 1 || d->num_q_heads != kGroup * d->num_kv_heads)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "num_q_heads %d must be 8 x num_kv_heads %d", d->num_q_heads,
+                d->num_kv_heads);
+  if (d->layout == GPTOSS_THD) {
+    if (d->batch > 0 && !d->cu_seqlens) return fail(GPTOSS_ERR_NULL, "THD layout needs cu_seqlens");
+    if (d->max_seqlen < 0 || d->max_seqlen > d->seqlen)
+      return fail(GPTOSS_ERR_SHAPE, "max_seqlen %d must be in [0, total tokens %d]", d->max_seqlen, d->seqlen);
+    if (d->batch > 4096) return fail(GPTOSS_ERR_UNSUPPORTED, "at most 4096 packed sequences");
+    if (d->max_seqlen > 8192 * kPrefillBQ)
+      return fail(GPTOSS_ERR_UNSUPPORTED, "packed sequences longer than %d tokens", 8192 * kPrefillBQ);
+  }
+  return GPTOSS_OK;
+}
+
+int32_t desc_max_len(const gptoss_seq_desc* d) { return d->layout == GPTOSS_BSHD ? d->seqlen : d->max_seqlen; }
+int64_t desc_tokens(const gptoss_seq_desc* d) {
+  return d->layout == GPTOSS_BSHD ? (int64_t)d->batch * d->seqlen : (int64_t)d->seqlen;
+}
+int32_t thd_max_items(const gptoss_seq_desc* d) {
+  return (d->seqlen + kPrefillBQ - 1) / kPrefillBQ + d->batch;
+}
+
+gptoss_status check_table(const void* table, int32_t table_rows, int32_t rotary_dim, int32_t need_rows) {
+  if (!table) return GPTOSS_OK;
+  if (rotary_dim != kHeadDim)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "rotary_dim %d unsupported (only 64 = head_dim)", rotary_dim);
+  if (!aligned16(table)) return fail(GPTOSS_ERR_UNSUPPORTED, "table must be 16-byte aligned");
+  if (table_rows < need_rows || table_rows < 1)
+    return fail(GPTOSS_ERR_SHAPE, "table has %d rows, positions up to %d are needed", table_rows, need_rows - 1);
+  return GPTOSS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gptoss_abi_version(void) { return GPTOSS_ABI_VERSION; }
+
+const char* gptoss_status_string(int status) {
+  switch (status) {
+    case GPTOSS_OK: return "ok";
+    case GPTOSS_ERR_NULL: return "null pointer argument";
+    case GPTOSS_ERR_SHAPE: return "inconsistent shape, stride or size";
+    case GPTOSS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GPTOSS_ERR_WORKSPACE: return "workspace missing or too small";
+    case GPTOSS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* gptoss_last_error(void) { return g_last_error.c_str(); }
+
+gptoss_status gptoss_yarn_params(const gptoss_rope_config* cfg, double* omega_out, double* concentration_out) {
+  double omega[kMaxPairs], c;
+  gptoss_status st = yarn(cfg, omega, &c);
+  if (st != GPTOSS_OK) return st;
+  if (omega_out) memcpy(omega_out, omega, sizeof(double) * (cfg->rotary_dim / 2));
+  if (concentration_out) *concentration_out = c;
+  return GPTOSS_OK;
+}
+
+gptoss_status gptoss_rope_table_init(const gptoss_rope_config* cfg, int32_t num_positions, void* table,
+                                     void* stream) {
+  if (!table) return fail(GPTOSS_ERR_NULL, "table is NULL");
+  if (num_positions < 1) return fail(GPTOSS_ERR_SHAPE, "num_positions must be >= 1");
+  TableParams p;
+  gptoss_status st = yarn(cfg, p.omega, &p.concentration);
+  if (st != GPTOSS_OK) return st;
+  p.half = cfg->rotary_dim / 2;
+  p.num_positions = num_positions;
+  p.table = static_cast<uint16_t*>(table);
+  return hip_status(launch_rope_table(p, static_cast<hipStream_t>(stream)), "rope table kernel");
+}
+
+gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
+                             const void* k, const int64_t k_strides[3], void* q_out, void* k_out,
+                             const void* table, int32_t table_rows, int32_t rotary_dim, void* stream) {
+  gptoss_status st = check_desc(desc);
+  if (st != GPTOSS_OK) return st;
+  if (desc_tokens(desc) == 0) return GPTOSS_OK;
+  if (!q || !k || !q_out || !k_out || !q_strides || !k_strides || !table)
+    return fail(GPTOSS_ERR_NULL, "q, k, q_out, k_out, strides and table are required");
+  if (!strides_ok(q_strides, 3) || !strides_ok(k_strides, 3) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(q_out) || !aligned16(k_out))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
+  st = check_table(table, table_rows, rotary_dim, desc_max_len(desc));
+  if (st != GPTOSS_OK) return st;
+  const bool thd = desc->layout == GPTOSS_THD;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int which = 0; which < 2; ++which) {
+    RopeQKParams p;
+    p.x = static_cast<const uint16_t*>(which ? k : q);
+    const int64_t* st3 = which ? k_strides : q_strides;
+    p.s_b = thd ? 0 : st3[0];
+    p.s_t = st3[1];
+    p.s_h = st3[2];
+    p.y = static_cast<uint16_t*>(which ? k_out : q_out);
+    p.batch = thd ? 1 : desc->batch;
+    p.tokens = desc->seqlen;
+    p.heads = which ? desc->num_kv_heads : desc->num_q_heads;
+    p.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
+    p.num_seqs = desc->batch;
+    p.table = static_cast<const uint16_t*>(table);
+    p.table_rows = table_rows;
+    if (thd && desc->batch == 0) return GPTOSS_OK;
+    st = hip_status(launch_rope_qk(p, s), "rope_qk kernel");
+    if (st != GPTOSS_OK) return st;
+  }
+  return GPTOSS_OK;
+}
+
+size_t gptoss_attn_prefill_workspace_size(const gptoss_seq_desc* desc) {
+  if (check_desc(desc) != GPTOSS_OK) return 0;
+  size_t bytes = 0;
+  if (desc->layout == GPTOSS_THD) bytes += round_up((size_t)thd_max_items(desc) * sizeof(int2)) + kAlign;
+  // rotated K when k is rotated by a separate pass
+  bytes += round_up((size_t)desc_tokens(desc) * desc->num_kv_heads * kHeadDim * sizeof(uint16_t));
+  return bytes;
+}
+
+}  // extern "C"
+
+namespace {
+gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
+                           const void* k, const int64_t k_strides[3], const void* v,
+                           const int64_t v_strides[3], const float* sinks, float softmax_scale,
+                           int32_t window, const void* table, int32_t table_rows, int32_t rotary_dim,
+                           void* out, const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
+                           int krot, void* stream) {
+  gptoss_status st = check_desc(desc);
+  if (st != GPTOSS_OK) return st;
+  if (desc_tokens(desc) == 0 || desc->batch == 0) return GPTOSS_OK;
+  if (!q || !k || !v || !out || !sinks || !q_strides || !k_strides || !v_strides || !o_strides)
+    return fail(GPTOSS_ERR_NULL, "q, k, v, out, sinks and all strides are required");
+  if (!strides_ok(q_strides, 3) || !strides_ok(k_strides, 3) || !strides_ok(v_strides, 3) ||
+      !strides_ok(o_strides, 3) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
+  if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  st = check_table(table, table_rows, rotary_dim, desc_max_len(desc));
+  if (st != GPTOSS_OK) return st;
+  const size_t need = gptoss_attn_prefill_workspace_size(desc);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return fail(GPTOSS_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  const bool thd = desc->layout == GPTOSS_THD;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  PrefillParams p;
+  memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_sb = thd ? 0 : q_strides[0]; p.q_st = q_strides[1]; p.q_sh = q_strides[2];
+  p.k = static_cast<const uint16_t*>(k);
+  p.k_sb = thd ? 0 : k_strides[0]; p.k_st = k_strides[1]; p.k_sh = k_strides[2];
+  p.v = static_cast<const uint16_t*>(v);
+  p.v_sb = thd ? 0 : v_strides[0]; p.v_st = v_strides[1]; p.v_sh = v_strides[2];
+  p.o = static_cast<uint16_t*>(out);
+  p.o_sb = thd ? 0 : o_strides[0]; p.o_st = o_strides[1]; p.o_sh = o_strides[2];
+  p.sinks = sinks;
+  p.table = static_cast<const uint16_t*>(table);
+  p.table_rows = table_rows;
+  p.batch = desc->batch;
+  p.seqlen = desc->seqlen;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.window = window;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
+
+  if (thd) {
+    const int32_t max_items = thd_max_items(desc);
+    int2* work = reinterpret_cast<int2*>(ws);
+    ws += round_up((size_t)max_items * sizeof(int2));
+    int32_t* count = reinterpret_cast<int32_t*>(ws);
+    ws += kAlign;
+    st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, max_items, work, count, s),
+                    "THD schedule kernel");
+    if (st != GPTOSS_OK) return st;
+    p.work = work;
+    p.work_count = count;
+    p.q_blocks = max_items;
+  } else {
+    p.q_blocks = (desc->seqlen + kPrefillBQ - 1) / kPrefillBQ;
+  }
+
+  if (table && krot != KROT_FUSED) {
+    // rotate k once into the workspace (contiguous), then attend with pre-rotated k
+    uint16_t* krot_buf = reinterpret_cast<uint16_t*>(ws);
+    RopeQKParams r;
+    r.x = static_cast<const uint16_t*>(k);
+    r.s_b = p.k_sb; r.s_t = p.k_st; r.s_h = p.k_sh;
+    r.y = krot_buf;
+    r.batch = thd ? 1 : desc->batch;
+    r.tokens = desc->seqlen;
+    r.heads = desc->num_kv_heads;
+    r.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
+    r.num_seqs = desc->batch;
+    r.table = p.table;
+    r.table_rows = table_rows;
+    st = hip_status(launch_rope_qk(r, s), "k rotation kernel");
+    if (st != GPTOSS_OK) return st;
+    p.k = krot_buf;
+    p.k_sh = kHeadDim;
+    p.k_st = (int64_t)desc->num_kv_heads * kHeadDim;
+    p.k_sb = thd ? 0 : (int64_t)desc->seqlen * p.k_st;
+  }
+  return hip_status(launch_prefill(p, thd, krot, s), "prefill kernel");
+}
+}  // namespace
+
+extern "C" {
+
+gptoss_status gptoss_attn_prefill(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
+                                  const void* k, const int64_t k_strides[3], const void* v,
+                                  const int64_t v_strides[3], const float* sinks, float softmax_scale,
+                                  int32_t window, const void* table, int32_t table_rows, int32_t rotary_dim,
+                                  void* out, const int64_t o_strides[3], void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  // K rotation: fused into the tile loads for window layers (few tiles per
+  // query block); one separate pass for full-causal layers, where every key
+  // tile is visited by many query blocks.
+  const int krot = window > 0 ? KROT_FUSED : KROT_NONE;
+  return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, sinks, softmax_scale, window, table,
+                      table_rows, rotary_dim, out, o_strides, workspace, workspace_bytes, krot, stream);
+}
+
+gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
+                                     const void* k, const int64_t k_strides[3], const void* v,
+                                     const int64_t v_strides[3], const float* sinks, float softmax_scale,
+                                     int32_t window, const void* table, int32_t table_rows,
+                                     int32_t rotary_dim, void* out, const int64_t o_strides[3],
+                                     void* workspace, size_t workspace_bytes, int32_t k_rotation,
+                                     void* stream) {
+  int krot;
+  switch (k_rotation) {
+    case GPTOSS_KROT_AUTO: krot = window > 0 ? KROT_FUSED : KROT_NONE; break;
+    case GPTOSS_KROT_FUSED: krot = KROT_FUSED; break;
+    case GPTOSS_KROT_SEPARATE: krot = KROT_NONE; break;
+    default: return fail(GPTOSS_ERR_SHAPE, "k_rotation %d is not a gptoss_k_rotation value", k_rotation);
+  }
+  return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, sinks, softmax_scale, window, table,
+                      table_rows, rotary_dim, out, o_strides, workspace, workspace_bytes, krot, stream);
+}
+
+// Keys per split: a multiple of 128 (4 waves x 32-key steps). Automatic: up to
+// 512 keys per work group, which gives thousands of work groups for long caches.
+static int32_t decode_chunk(int32_t eff_len, int32_t num_splits) {
+  int32_t c = num_splits > 0 ? (eff_len + num_splits - 1) / num_splits : (eff_len < 512 ? eff_len : 512);
+  c = (c + 127) / 128 * 128;
+  return c < 128 ? 128 : c;
+}
+
+// Upper bound of the splits any call with these sizes uses (window layers use fewer).
+static int64_t decode_split_cap(int32_t max_cache_len, int32_t num_splits) {
+  return num_splits > 0 ? num_splits : (max_cache_len + 511) / 512;
+}
+
+size_t gptoss_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_cache_len,
+                                         int32_t num_splits) {
+  if (num_seqs < 0 || num_q_heads < 0 || max_cache_len < 1 || num_splits < 0) return 0;
+  const size_t slots = (size_t)num_seqs * num_q_heads * decode_split_cap(max_cache_len, num_splits);
+  return round_up(slots * kHeadDim * sizeof(float)) + round_up(slots * 2 * sizeof(float));
+}
+
+gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 const void* q, const int64_t q_strides[2], const void* k_cache,
+                                 const void* v_cache, const int64_t kv_strides[3],
+                                 const int32_t* cache_seqlens, int32_t max_cache_len, const float* sinks,
+                                 float softmax_scale, int32_t window, const void* table, int32_t table_rows,
+                                 int32_t rotary_dim, void* out, const int64_t o_strides[2], void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
+  if (num_seqs < 0) return fail(GPTOSS_ERR_SHAPE, "num_seqs must be >= 0");
+  if (head_dim != kHeadDim) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", head_dim);
+  if (num_kv_heads < 1 || num_q_heads != kGroup * num_kv_heads)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "num_q_heads %d must be 8 x num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (max_cache_len < 1) return fail(GPTOSS_ERR_SHAPE, "max_cache_len must be >= 1");
+  if (num_splits < 0) return fail(GPTOSS_ERR_SHAPE, "num_splits must be >= 0");
+  if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (num_seqs == 0) return GPTOSS_OK;
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !sinks || !out || !q_strides || !kv_strides || !o_strides)
+    return fail(GPTOSS_ERR_NULL, "q, caches, cache_seqlens, sinks, out and all strides are required");
+  if (!strides_ok(q_strides, 2) || !strides_ok(kv_strides, 3) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
+  if (o_strides[0] < 0 || o_strides[1] < 0 || (o_strides[0] & 1) || (o_strides[1] & 1) ||
+      (reinterpret_cast<uintptr_t>(out) & 3))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "out must be 4-byte aligned with even strides");
+  gptoss_status st = check_table(table, table_rows, rotary_dim, max_cache_len);
+  if (st != GPTOSS_OK) return st;
+  const size_t need = gptoss_attn_decode_workspace_size(num_seqs, num_q_heads, max_cache_len, num_splits);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return fail(GPTOSS_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  DecodeParams p;
+  memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_sn = q_strides[0]; p.q_sh = q_strides[1];
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.kv_sn = kv_strides[0]; p.kv_sp = kv_strides[1]; p.kv_sh = kv_strides[2];
+  p.cache_seqlens = cache_seqlens;
+  p.max_cache_len = max_cache_len;
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = num_kv_heads;
+  p.window = window;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.sinks = sinks;
+  p.table = static_cast<const uint16_t*>(table);
+  p.table_rows = table_rows;
+  // window layers only ever read the last `window` rows: smaller chunks, fewer splits
+  const int32_t eff = (window > 0 && window < max_cache_len) ? window : max_cache_len;
+  p.chunk = decode_chunk(eff, num_splits);
+  p.num_splits = (eff + p.chunk - 1) / p.chunk;   // <= decode_split_cap(): fits the workspace
+  char* ws = static_cast<char*>(workspace);
+  const size_t slots = (size_t)num_seqs * num_q_heads * p.num_splits;
+  p.part_o = reinterpret_cast<float*>(ws);
+  p.part_ml = reinterpret_cast<float*>(ws + round_up(slots * kHeadDim * sizeof(float)));
+  p.o = static_cast<uint16_t*>(out);
+  p.o_sn = o_strides[0]; p.o_sh = o_strides[1];
+  return hip_status(launch_decode(p, static_cast<hipStream_t>(stream)), "decode kernels");
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Device helpers shared by the gfx950 kernels: bf16 packing, the exactly
+// rounded RoPE pair rotation, MFMA fragment types and LDS transpose reads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptoss {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round two fp32 values to bf16 (nearest-even, hardware v_cvt_pk_bf16_f32) and pack.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// RoPE rotation of one half-split pair, rounded once to bf16.
+//
+// y1 = x1*C - x2*S and y2 = x2*C + x1*S with bf16 x1, x2, C, S. Each product of
+// two bf16 values has at most 16 significant bits, so it is exact in fp32
+// (barring fp32 underflow below 2^-126). One fma then yields y correctly
+// rounded to fp32. Rounding that fp32 value to bf16 can only differ from
+// rounding the exact value once when the fp32 result sits exactly on a bf16
+// midpoint (low 16 bits == 0x8000) while the exact value does not; then the
+// fp32 value is moved one fp32 ulp towards the exact value, which is below or
+// above the midpoint by the sign of the fma's rounding error e (found with
+// the TwoSum error-free transformation). The result equals the exact value
+// rounded once to bf16 (nearest-even).
+// ---------------------------------------------------------------------------
+#pragma clang fp contract(off)
+__device__ __forceinline__ float two_sum_err(float a, float b, float s) {
+  float bb = s - a;
+  return (a - (s - bb)) + (b - bb);
+}
+#pragma clang fp contract(on)
+
+// Exact-rounding fix-up of s = RN_fp32(a + b) where a and b are exact fp32 values.
+__device__ __forceinline__ float fix_bf16_tie(float a, float b, float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0xFFFFu) == 0x8000u) {
+    float e = two_sum_err(a, b, s);
+    if (e != 0.0f) u += ((e > 0.0f) == (s > 0.0f)) ? 1u : 0xFFFFFFFFu;
+  }
+  return __uint_as_float(u);
+}
+
+// Rotate 8 pairs: x1 holds dims i..i+7, x2 dims i+32..i+39 (rotary_dim 64),
+// c / s the table's cos / sin for the same i. Writes rounded bf16 outputs.
+__device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const uint4& c,
+                                      const uint4& s, uint4& y1, uint4& y2) {
+  const uint32_t* px1 = reinterpret_cast<const uint32_t*>(&x1);
+  const uint32_t* px2 = reinterpret_cast<const uint32_t*>(&x2);
+  const uint32_t* pc = reinterpret_cast<const uint32_t*>(&c);
+  const uint32_t* ps = reinterpret_cast<const uint32_t*>(&s);
+  uint32_t* py1 = reinterpret_cast<uint32_t*>(&y1);
+  uint32_t* py2 = reinterpret_cast<uint32_t*>(&y2);
+  float r1[8], r2[8];
+  bool tie = false;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float a1 = h ? bf16_hi(px1[w]) : bf16_lo(px1[w]);
+      float a2 = h ? bf16_hi(px2[w]) : bf16_lo(px2[w]);
+      float cc = h ? bf16_hi(pc[w]) : bf16_lo(pc[w]);
+      float ss = h ? bf16_hi(ps[w]) : bf16_lo(ps[w]);
+      float t1 = a2 * ss;                      // exact
+      float t2 = a1 * ss;                      // exact
+      float o1 = __builtin_fmaf(a1, cc, -t1);  // RN(x1*C - x2*S)
+      float o2 = __builtin_fmaf(a2, cc, t2);   // RN(x2*C + x1*S)
+      r1[2 * w + h] = o1;
+      r2[2 * w + h] = o2;
+      tie = tie || ((__float_as_uint(o1) & 0xFFFFu) == 0x8000u) || ((__float_as_uint(o2) & 0xFFFFu) == 0x8000u);
+    }
+  }
+  if (tie) {  // rare: redo the affected elements with the exact fix-up
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float a1 = h ? bf16_hi(px1[w]) : bf16_lo(px1[w]);
+        float a2 = h ? bf16_hi(px2[w]) : bf16_lo(px2[w]);
+        float cc = h ? bf16_hi(pc[w]) : bf16_lo(pc[w]);
+        float ss = h ? bf16_hi(ps[w]) : bf16_lo(ps[w]);
+        r1[2 * w + h] = fix_bf16_tie(a1 * cc, -(a2 * ss), r1[2 * w + h]);
+        r2[2 * w + h] = fix_bf16_tie(a2 * cc, a1 * ss, r2[2 * w + h]);
+      }
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    py1[w] = pack_bf16x2(r1[2 * w], r1[2 * w + 1]);
+    py2[w] = pack_bf16x2(r2[2 * w], r2[2 * w + 1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA v_mfma_f32_16x16x32_bf16 (one wave of 64 lanes):
+//   A[i][k]: lane i + 16*(k/8), element k%8     (16 rows x 32 k)
+//   B[k][n]: lane n + 16*(k/8), element k%8     (32 k x 16 cols)
+//   D[i][n]: lane n + 16*(i/4), element i%4     (16 x 16, fp32)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives in slot j the
+// (i % 4)-th 16-bit element of the 8-byte chunk addressed by lane 4*j + i/4 of
+// the same group.
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  // A C-style cast from the generic pointer emits an addrspacecast to LDS.
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void stg16(bf16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace gptoss

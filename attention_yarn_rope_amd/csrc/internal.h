@@ -1,0 +1,80 @@
+// Internal interface between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptoss {
+
+constexpr int kHeadDim = 64;     // D: the only head width the kernels are built for
+constexpr int kGroup = 8;        // query heads per KV head (64 / 8 in GPT-OSS)
+constexpr int kMaxPairs = 32;    // rotary_dim / 2
+
+// ---- RoPE table ----
+struct TableParams {
+  double omega[kMaxPairs];
+  double concentration;
+  int32_t half;                  // rotary_dim / 2
+  int32_t num_positions;
+  uint16_t* table;               // [num_positions, 2*half]
+};
+hipError_t launch_rope_table(const TableParams& p, hipStream_t stream);
+
+// ---- standalone q/k rotation ----
+struct RopeQKParams {
+  const uint16_t* x;             // one tensor (q or k)
+  int64_t s_b, s_t, s_h;         // element strides of batch, token, head
+  uint16_t* y;                   // contiguous output [.., tokens, heads, 64]
+  int32_t batch, tokens, heads;  // BSHD: batch x seqlen; THD: batch = 1, tokens = T
+  const int32_t* cu_seqlens;     // THD positions (NULL for BSHD)
+  int32_t num_seqs;
+  const uint16_t* table;
+  int32_t table_rows;
+};
+hipError_t launch_rope_qk(const RopeQKParams& p, hipStream_t stream);
+
+// ---- prefill ----
+struct PrefillParams {
+  const uint16_t* q; int64_t q_sb, q_st, q_sh;
+  const uint16_t* k; int64_t k_sb, k_st, k_sh;
+  const uint16_t* v; int64_t v_sb, v_st, v_sh;
+  uint16_t* o; int64_t o_sb, o_st, o_sh;
+  const float* sinks;
+  const uint16_t* table;         // NULL: q (and k) already rotated
+  int32_t table_rows;
+  int32_t batch;                 // BSHD batch, or number of THD sequences
+  int32_t seqlen;                // BSHD S, or THD total tokens
+  int32_t num_kv_heads;
+  int32_t window;
+  float scale_log2;              // softmax_scale * log2(e)
+  int32_t q_blocks;              // BSHD: ceil(S / BQ); THD: max work items per KV head
+  const int32_t* cu_seqlens;     // THD
+  const int2* work;              // THD work list (seq, q block), longest first
+  const int32_t* work_count;     // THD: number of valid entries in `work`
+};
+enum KRotation { KROT_NONE = 0, KROT_FUSED = 1 };
+hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_t stream);
+hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_items,
+                               int2* work, int32_t* work_count, hipStream_t stream);
+constexpr int kPrefillBQ = 32;   // query positions per work item
+
+// ---- decode ----
+struct DecodeParams {
+  const uint16_t* q; int64_t q_sn, q_sh;
+  const uint16_t* k; const uint16_t* v; int64_t kv_sn, kv_sp, kv_sh;
+  const int32_t* cache_seqlens;
+  int32_t max_cache_len;
+  int32_t num_seqs, num_kv_heads;
+  int32_t window;
+  float scale_log2;
+  const float* sinks;
+  const uint16_t* table;
+  int32_t table_rows;
+  int32_t num_splits, chunk;     // keys per split (multiple of 128)
+  float* part_o;                 // [N, Hkv, splits, 8, 64]
+  float* part_ml;                // [N, Hkv, splits, 8, 2]
+  uint16_t* o; int64_t o_sn, o_sh;
+};
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace gptoss

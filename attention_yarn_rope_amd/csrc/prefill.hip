@@ -1,0 +1,395 @@
+// Flash-style prefill attention for GPT-OSS on gfx950: learned per-head sink,
+// grouped-query attention (8 query heads per KV head), causal or sliding-window
+// mask, YaRN RoPE applied while q and k tiles are loaded.
+//
+// What is computed (page "nemo_automodel.components.models.gpt_oss.layers",
+// GptOssAttention: sinks, sliding_window, softmax_scale = head_dim ** -0.5;
+// Transformers v4.55.0 release notes, "Architecture": alternating full-context
+// and sliding 128-token-window layers, a per-head sink adding a term to the
+// softmax denominator):
+//   o[i,h] = sum_{j visible} exp(s_ij - M) v[j,g] / (exp(sigma_h - M) + sum_{j visible} exp(s_ij - M))
+// with s_ij = tau <q~_i, k~_j>, g = h / 8, visible: j <= i and (W == 0 or i - j < W).
+//
+// Work item: (sequence, KV head g, block of BQ = 32 query positions). Its 256
+// query rows are the 8 heads of group g x 32 positions, so every K/V tile is
+// read from HBM once and staged in LDS once for the whole GQA group. Each of the
+// 4 waves owns 64 query rows (2 heads x 32 positions) as four 16-column blocks.
+// Per KV tile of 64 keys a wave runs 32 MFMAs for S^T = K Q^T and 32 for
+// O^T = V^T P^T (v_mfma_f32_16x16x32_bf16, fp32 accumulation). The softmax
+// runs on S^T, whose accumulator layout is already the B-operand layout P^T
+// needs (keys permuted consistently between V^T and P^T). V^T comes straight
+// from the row-major V tile in LDS through ds_read_b64_tr_b16.
+//
+// Online softmax in log2 units, seeded with the sink: m = sigma_h*log2(e),
+// l = 1. The running reference m is only raised when a tile's maximum exceeds
+// it by more than 8 (p stays <= 2^8, safe in fp32 and bf16), which skips the
+// rescale of the accumulator on almost every tile; the result is the same
+// ratio. Tiles fully visible to every query of the item skip the mask; tiles
+// fully hidden are never visited.
+#include "common.h"
+#include "internal.h"
+
+namespace gptoss {
+namespace {
+
+constexpr int BQ = kPrefillBQ;  // 32 query positions per item
+constexpr int NK = 64;          // keys per KV tile
+constexpr int NT = 256;         // threads per work group (4 waves)
+constexpr int KS = 72;          // LDS row stride of the K tile (144 B): conflict-free 16 B reads
+constexpr int VS = 80;          // LDS row stride of the V tile (160 B): conflict-free tr16 reads
+constexpr float kRescaleGap = 8.0f;
+
+__device__ __forceinline__ float wave_xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_xor_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <bool ROTQ, bool ROTK, bool THD>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds_k[2][NK * KS];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_v[2][NK * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;   // MFMA column (query) / row (key, d) inside a 16-block
+  const int grp = lane >> 4;   // 16-lane group
+
+  // ---- work item: consecutive blocks take consecutive KV heads, so with 8 KV
+  // heads every XCD (blocks are dealt round-robin over the 8 XCDs) serves one
+  // KV head and keeps its K/V in its own L2.
+  const int Hkv = p.num_kv_heads;
+  const int item = blockIdx.x / Hkv;
+  const int g = blockIdx.x - item * Hkv;
+  int j, L;
+  int64_t bb_off_q, bb_off_k, bb_off_v, bb_off_o;  // batch offsets
+  int ts;                                          // first token of the sequence
+  if (THD) {
+    if (item >= __ldg(p.work_count)) return;
+    const int2 w = p.work[item];
+    j = w.y;
+    const int n = min(max(w.x, 0), p.batch - 1);
+    ts = min(max(__ldg(p.cu_seqlens + n), 0), p.seqlen);
+    const int te = min(max(__ldg(p.cu_seqlens + n + 1), ts), p.seqlen);
+    L = te - ts;
+    bb_off_q = bb_off_k = bb_off_v = bb_off_o = 0;
+  } else {
+    const int r = item / p.batch;
+    const int b = item - r * p.batch;
+    j = p.q_blocks - 1 - r;     // longest (most keys) first
+    ts = 0;
+    L = p.seqlen;
+    bb_off_q = b * p.q_sb; bb_off_k = b * p.k_sb; bb_off_v = b * p.v_sb; bb_off_o = b * p.o_sb;
+  }
+  const int q0 = j * BQ;
+  if (j < 0 || q0 >= L) return;
+  const int qlast = min(q0 + BQ, L) - 1;
+  const int W = p.window;
+  const uint32_t weff = (W > 0) ? (uint32_t)W : 0x7FFFFFFFu;   // keys visible: 0 <= qpos - kpos < weff
+  const int kv_lo = (W > 0) ? max(0, q0 - W + 1) : 0;
+  const int kv_hi = qlast + 1;
+  const int ntiles = (kv_hi - kv_lo + NK - 1) / NK;
+  const float sl = p.scale_log2;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), rotated on load ----
+  bf16x8_t qf[4][2];
+  int qpos[2];
+  qpos[0] = q0 + col;
+  qpos[1] = q0 + 16 + col;
+  float m[4], lsum[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int head = g * kGroup + wave * 2 + (cb >> 1);
+    const int pos = qpos[cb & 1];
+    uint4 y1 = make_uint4(0, 0, 0, 0), y2 = make_uint4(0, 0, 0, 0);
+    if (pos <= qlast) {
+      const bf16_t* qp = p.q + bb_off_q + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh;
+      uint4 x1 = ldg16(qp + 8 * grp), x2 = ldg16(qp + 32 + 8 * grp);
+      if (ROTQ) {
+        const bf16_t* tp = p.table + (int64_t)min(pos, p.table_rows - 1) * kHeadDim + 8 * grp;
+        rope8(x1, x2, ldg16(tp), ldg16(tp + 32), y1, y2);
+      } else {
+        y1 = x1; y2 = x2;
+      }
+    }
+    qf[cb][0] = as_bf16x8(y1);
+    qf[cb][1] = as_bf16x8(y2);
+    const float sink = __ldg(p.sinks + head);
+    m[cb] = sink * kLog2e;              // -inf stays -inf
+    lsum[cb] = (grp == 0) ? 1.0f : 0.0f;  // the sink's exp(sigma - m) = 1, counted once
+  }
+
+  f32x4_t oacc[4][4];  // [d block][column block]
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) oacc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // ---- K/V tile staging: thread -> (row, 8-dim chunk cc and cc + 4) ----
+  const int srow = tid >> 2;
+  const int scc = tid & 3;
+  uint4 sk1, sk2, sv1, sv2, sc, ss;
+  auto load_tile = [&](int t) {
+    const int kpos = kv_lo + t * NK + srow;
+    if (kpos < kv_hi) {
+      const int64_t tok = ts + kpos;
+      const bf16_t* kp = p.k + bb_off_k + tok * p.k_st + (int64_t)g * p.k_sh + 8 * scc;
+      const bf16_t* vp = p.v + bb_off_v + tok * p.v_st + (int64_t)g * p.v_sh + 8 * scc;
+      sk1 = ldg16(kp); sk2 = ldg16(kp + 32);
+      sv1 = ldg16(vp); sv2 = ldg16(vp + 32);
+      if (ROTK) {
+        const bf16_t* tp = p.table + (int64_t)min(kpos, p.table_rows - 1) * kHeadDim + 8 * scc;
+        sc = ldg16(tp); ss = ldg16(tp + 32);
+      }
+    } else {
+      sk1 = sk2 = sv1 = sv2 = make_uint4(0, 0, 0, 0);
+      sc = ss = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint4 k1 = sk1, k2 = sk2;
+    if (ROTK) rope8(sk1, sk2, sc, ss, k1, k2);
+    bf16_t* kd = &lds_k[buf][srow * KS + 8 * scc];
+    bf16_t* vd = &lds_v[buf][srow * VS + 8 * scc];
+    *reinterpret_cast<uint4*>(kd) = k1;
+    *reinterpret_cast<uint4*>(kd + 32) = k2;
+    *reinterpret_cast<uint4*>(vd) = sv1;
+    *reinterpret_cast<uint4*>(vd + 32) = sv2;
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const int tile0 = kv_lo + t * NK;
+    const bf16_t* kt = lds_k[buf];
+    const bf16_t* vt = lds_v[buf];
+
+    // ---- S^T = K Q^T: sacc[kb][cb] element r = key (kb*16 + 4*grp + r), query col ----
+    f32x4_t sacc[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16_t* krow = kt + (kb * 16 + col) * KS + 8 * grp;
+      const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(krow));
+      const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32));
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        z = mfma16(a0, qf[cb][0], z);
+        sacc[kb][cb] = mfma16(a1, qf[cb][1], z);
+      }
+    }
+
+    // ---- mask: only tiles that are not fully visible to every query of the item.
+    // visible <=> 0 <= qpos - kpos < weff, one unsigned compare (branch free) ----
+    const bool full = (tile0 + NK - 1 <= q0) && (W == 0 || qlast - tile0 < W);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kpos = tile0 + kb * 16 + 4 * grp + r;
+          const bool vis0 = (uint32_t)(qpos[0] - kpos) < weff;
+          const bool vis1 = (uint32_t)(qpos[1] - kpos) < weff;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const bool vis = (cb & 1) ? vis1 : vis0;
+            sacc[kb][cb][r] = vis ? sacc[kb][cb][r] : -INFINITY;
+          }
+        }
+    }
+
+    // ---- online softmax (log2 units), lazy rescale ----
+    float mx[4];
+    bool need = false;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      float v = sacc[0][cb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v = fmaxf(v, sacc[kb][cb][r]);
+      mx[cb] = v * sl;
+      need |= mx[cb] > m[cb] + kRescaleGap;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const float mt = wave_xor_max(mx[cb]);
+        if (mt > m[cb] + kRescaleGap) {   // uniform across the 4 lanes of the column
+          const float f = __builtin_amdgcn_exp2f(m[cb] - mt);   // m = -inf -> 0
+          lsum[cb] *= f;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) oacc[db][cb] *= f;
+          m[cb] = mt;
+        }
+      }
+    }
+
+    bf16x8_t pf[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const float mu = (m[cb] == -INFINITY) ? 0.0f : m[cb];
+      uint32_t w[8];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][0], sl, -mu));
+        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][1], sl, -mu));
+        float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][2], sl, -mu));
+        float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][3], sl, -mu));
+        w[2 * kb] = pack_bf16x2(e0, e1);
+        w[2 * kb + 1] = pack_bf16x2(e2, e3);
+      }
+      // row sum of the bf16-rounded probabilities actually used by PV
+      float s = lsum[cb];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += bf16_lo(w[i]) + bf16_hi(w[i]);
+      lsum[cb] = s;
+      // keys pi(grp, e): e < 4 -> 4*grp + e of key block 2ks, e >= 4 -> of key block 2ks+1
+      pf[cb][0] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      pf[cb][1] = __builtin_bit_cast(bf16x8_t, make_uint4(w[4], w[5], w[6], w[7]));
+    }
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16_t* vb = vt + (32 * ks + 4 * grp + (col >> 2)) * VS + 16 * db + 4 * (col & 3);
+        const uint2 lo = lds_read_tr16(vb);
+        const uint2 hi = lds_read_tr16(vb + 16 * VS);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) oacc[db][cb] = mfma16(a, pf[cb][ks], oacc[db][cb]);
+      }
+    }
+
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: o = acc / l, bf16 store; lane holds d = 16*db + 4*grp + r ----
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const float l = wave_xor_sum(lsum[cb]);
+    const int pos = qpos[cb & 1];
+    if (pos > qlast) continue;
+    const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+    const int head = g * kGroup + wave * 2 + (cb >> 1);
+    bf16_t* op = p.o + bb_off_o + (int64_t)(ts + pos) * p.o_st + (int64_t)head * p.o_sh + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      uint2 v;
+      v.x = pack_bf16x2(oacc[db][cb][0] * inv, oacc[db][cb][1] * inv);
+      v.y = pack_bf16x2(oacc[db][cb][2] * inv, oacc[db][cb][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * db) = v;
+    }
+  }
+}
+
+// Work list for packed sequences: every (sequence n, query block jb) with
+// jb < ceil(L_n / BQ), ordered by jb descending (the blocks with the most keys
+// first), sequences ascending within one jb. One work group of 1024 threads.
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedMaxBlocks = 8192;   // query blocks per sequence (L <= 262144)
+constexpr int kSchedMaxSeqs = 4096;
+
+__global__ __launch_bounds__(kSchedThreads) void thd_schedule_kernel(const int32_t* cu, int32_t num_seqs,
+                                                                     int32_t max_items, int2* work,
+                                                                     int32_t* work_count) {
+  __shared__ int32_t nb[kSchedMaxSeqs];
+  __shared__ int32_t cnt[kSchedMaxBlocks];
+  __shared__ int32_t part[kSchedThreads];
+  __shared__ int32_t jmax_s;
+  const int tid = threadIdx.x;
+  if (tid == 0) jmax_s = 0;
+  __syncthreads();
+  int local_max = 0;
+  for (int n = tid; n < num_seqs; n += kSchedThreads) {
+    const int a = __ldg(cu + n), b = __ldg(cu + n + 1);
+    const int len = max(b - a, 0);
+    const int q = min((len + BQ - 1) / BQ, kSchedMaxBlocks);
+    nb[n] = q;
+    local_max = max(local_max, q);
+  }
+  atomicMax(&jmax_s, local_max);
+  __syncthreads();
+  const int J = jmax_s;
+  // count[jb] = number of sequences with more than jb blocks
+  for (int jb = tid; jb < J; jb += kSchedThreads) {
+    int c = 0;
+    for (int n = 0; n < num_seqs; ++n) c += (nb[n] > jb);
+    cnt[jb] = c;
+  }
+  __syncthreads();
+  // start[jb] = sum of cnt[jb'] for jb' > jb: each thread owns a contiguous
+  // run of jb taken from the top, then an exclusive scan over the threads.
+  const int per = (J + kSchedThreads - 1) / kSchedThreads;
+  const int r0 = tid * per;                 // run in "from the top" order: rank = J-1-jb
+  int mysum = 0;
+  for (int r = r0; r < min(r0 + per, J); ++r) mysum += cnt[J - 1 - r];
+  part[tid] = mysum;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    const int v = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - mysum;              // exclusive prefix
+  for (int r = r0; r < min(r0 + per, J); ++r) {
+    const int jb = J - 1 - r;
+    const int c = cnt[jb];
+    int idx = run;
+    for (int n = 0; n < num_seqs; ++n) {
+      if (nb[n] > jb) {
+        if (idx < max_items) work[idx] = make_int2(n, jb);
+        ++idx;
+      }
+    }
+    run += c;
+  }
+  if (tid == kSchedThreads - 1) *work_count = min(part[kSchedThreads - 1], max_items);
+}
+
+template <bool ROTQ, bool ROTK, bool THD>
+hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.q_blocks * (THD ? 1 : p.batch) * p.num_kv_heads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD>), dim3((uint32_t)blocks), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_items,
+                               int2* work, int32_t* work_count, hipStream_t stream) {
+  hipLaunchKernelGGL(thd_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens, num_seqs,
+                     max_items, work, work_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_t stream) {
+  const bool rotq = p.table != nullptr;
+  const bool rotk = rotq && krot == KROT_FUSED;
+  if (thd) {
+    if (!rotq) return launch_one<false, false, true>(p, stream);
+    return rotk ? launch_one<true, true, true>(p, stream) : launch_one<true, false, true>(p, stream);
+  }
+  if (!rotq) return launch_one<false, false, false>(p, stream);
+  return rotk ? launch_one<true, true, false>(p, stream) : launch_one<true, false, false>(p, stream);
+}
+
+}  // namespace gptoss

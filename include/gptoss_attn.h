@@ -1,0 +1,237 @@
+/*
+ * gptoss_attn.h -- C ABI of the GPT-OSS attention hot path on MI355X (gfx950).
+ *
+ * Grouped-query attention with a learned per-head sink, full-causal or
+ * sliding-window masks, and YaRN-scaled RoPE on q and k; bf16 in and out,
+ * fp32 accumulation.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers unless marked "host". The library
+ *     never allocates, frees or copies device memory on its own and never
+ *     synchronises: the caller owns every buffer (inputs, outputs, table,
+ *     workspace) and keeps it alive until the work on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues kernels on it and returns.
+ *   - bf16 means IEEE bfloat16 stored as uint16; fp32 sinks.
+ *   - Strides are in ELEMENTS, not bytes; the last (head_dim) dimension must
+ *     be contiguous. Outputs of gptoss_rope_qk are contiguous; the attention
+ *     outputs take strides.
+ *   - Host-checkable argument errors return a non-zero gptoss_status before
+ *     anything is launched. A failed launch returns GPTOSS_ERR_HIP.
+ *     gptoss_last_error() gives a thread-local text for the last failure.
+ *     No C++ exception crosses this interface.
+ *   - Device-resident integer data (cu_seqlens, cache_seqlens) cannot be
+ *     checked without a synchronisation. It is trusted, and the kernels clamp
+ *     every index derived from it so that bad values cannot read or write
+ *     outside the buffers described by the host-side sizes.
+ *
+ * Supported now: head_dim == rotary_dim == 64, num_q_heads == 8 * num_kv_heads
+ * (the GPT-OSS grouping: 64 query heads over 8 KV heads); other shapes return
+ * GPTOSS_ERR_UNSUPPORTED.
+ */
+#ifndef GPTOSS_ATTN_H
+#define GPTOSS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPTOSS_ABI_VERSION 1
+
+typedef enum {
+  GPTOSS_OK = 0,
+  GPTOSS_ERR_NULL = 1,        /* a required pointer is NULL */
+  GPTOSS_ERR_SHAPE = 2,       /* sizes or strides are inconsistent or out of range */
+  GPTOSS_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. head_dim != 64) */
+  GPTOSS_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than *_workspace_size() */
+  GPTOSS_ERR_HIP = 5          /* a HIP launch or query failed; see gptoss_last_error() */
+} gptoss_status;
+
+typedef enum { GPTOSS_BSHD = 0, GPTOSS_THD = 1 } gptoss_layout;
+
+/*
+ * RoPE configuration: the RotaryEmbedding constructor on the page
+ * "nemo_automodel.components.models.gpt_oss.rope_utils" (head_dim, base,
+ * initial_context_length = 4096, scaling_factor = 1.0, ntk_alpha = 1.0,
+ * ntk_beta = 32.0, rotary_dim = head_dim * partial_rotary_factor).
+ * GPT-OSS: head_dim 64, rotary_dim 64, base 150000, scaling_factor 32.
+ */
+typedef struct {
+  int32_t head_dim;
+  int32_t rotary_dim;             /* even, 0 < rotary_dim <= head_dim */
+  double base;
+  double scaling_factor;          /* <= 1 means plain RoPE */
+  int32_t initial_context_length;
+  double ntk_alpha;               /* beta_slow of YaRN */
+  double ntk_beta;                /* beta_fast of YaRN */
+} gptoss_rope_config;
+
+/*
+ * Sequence description shared by gptoss_rope_qk and gptoss_attn_prefill.
+ * BSHD: tensors are [batch, seqlen, heads, head_dim]; every sequence has
+ *       length seqlen and token s sits at position s.
+ * THD:  tensors are packed [seqlen = total tokens, heads, head_dim]; sequence n
+ *       holds tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 and positions restart
+ *       at 0 in every sequence. `batch` is the number of sequences and
+ *       cu_seqlens a DEVICE int32 array of batch+1 entries, cu_seqlens[0] = 0,
+ *       non-decreasing, cu_seqlens[batch] = seqlen. `max_seqlen` is a host-side
+ *       upper bound of the sequence lengths (it sizes the grid).
+ * (page "nemo_automodel.components.models.gpt_oss.rope_utils",
+ *  apply_rotary_emb_qk: format "bshd" or "thd", cu_seqlens [num_sequences+1];
+ *  page "nemo_automodel.components.models.gpt_oss.model", GptOssForCausalLM
+ *  forward: BSHD or THD inputs.)
+ */
+typedef struct {
+  int32_t layout;                 /* gptoss_layout */
+  int32_t batch;                  /* B, or the number of packed sequences */
+  int32_t seqlen;                 /* S, or the total token count T */
+  int32_t max_seqlen;             /* BSHD: S; THD: >= every sequence length */
+  const int32_t* cu_seqlens;      /* THD only (device); NULL for BSHD */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+} gptoss_seq_desc;
+
+int gptoss_abi_version(void);
+const char* gptoss_status_string(int status);
+const char* gptoss_last_error(void);
+
+/*
+ * YaRN frequencies and concentration on the host (rope_utils page,
+ * RotaryEmbedding._compute_concentration_and_inv_freq, which follows the YaRN
+ * paper and works over rotary_dim; layers page, GptOssAttention.yarn_concentration).
+ *   omega_out:          host double[rotary_dim / 2], nullable
+ *   concentration_out:  host double, nullable
+ * omega_i blends theta_i = base^(-2i/rotary_dim) and theta_i / scaling_factor
+ * with a ramp linear in i between the dimensions that turn ntk_beta and
+ * ntk_alpha times over initial_context_length; the concentration is
+ * 0.1 ln(scaling_factor) + 1 (1 and plain RoPE when scaling_factor <= 1).
+ */
+gptoss_status gptoss_yarn_params(const gptoss_rope_config* cfg, double* omega_out,
+                                 double* concentration_out);
+
+/*
+ * The bf16 cos/sin table (rope_utils page, RotaryEmbedding._compute_cos_sin;
+ * _apply_rotary_emb_qk: cosine table concatenated with sine table, rounded
+ * to the q/k dtype, concentration applied).
+ *   table: device bf16 [num_positions, rotary_dim]; row p holds
+ *          c*cos(p*omega_i) for i < rotary_dim/2, then c*sin(p*omega_i).
+ *          Each entry is the fp64 value rounded once to bf16 (nearest-even);
+ *          the angle p*omega_i is formed in fp64.
+ * Errors: NULL cfg/table, num_positions < 1, bad rotary_dim.
+ */
+gptoss_status gptoss_rope_table_init(const gptoss_rope_config* cfg, int32_t num_positions,
+                                     void* table, void* stream);
+
+/*
+ * Rotate q and k together with one shared table, out of place
+ * (rope_utils page, _apply_rotary_emb_qk and apply_rotary_emb_qk).
+ *   q: bf16, BSHD [B, S, Hq, D] or THD [T, Hq, D]; q_strides[3] = element
+ *      strides of (batch, token, head) -- for THD q_strides[0] is ignored.
+ *   k: same with Hkv heads.
+ *   q_out, k_out: contiguous bf16 outputs of the same logical shapes.
+ *   table: from gptoss_rope_table_init, table_rows >= max position + 1.
+ * The pair (x[i], x[i + rotary_dim/2]) is multiplied as a complex number by
+ * (cos_i + j sin_i) of the token's position row; each output element is the
+ * exact result rounded once to bf16; dims >= rotary_dim are copied.
+ */
+gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc,
+                             const void* q, const int64_t q_strides[3],
+                             const void* k, const int64_t k_strides[3],
+                             void* q_out, void* k_out,
+                             const void* table, int32_t table_rows, int32_t rotary_dim,
+                             void* stream);
+
+/*
+ * Prefill attention with sink, GQA and a causal / sliding-window mask
+ * (layers page, GptOssAttention: sinks, sliding_window,
+ *  softmax_scale = head_dim ** -0.5; Transformers v4.55.0 release notes,
+ *  "Architecture": alternating full-context and sliding 128-token window
+ *  layers, a learned per-head sink that adds a term to the softmax
+ *  denominator).
+ *   q, k, v: bf16 in the desc's layout (strides as in gptoss_rope_qk).
+ *            With a table, q and k are the UN-rotated projections and are
+ *            rotated on the fly, bit-identically to gptoss_rope_qk; with
+ *            table == NULL they are taken as already rotated.
+ *   sinks:   device fp32 [num_q_heads]; sink logit of each query head, in the
+ *            units of the scaled scores (-INFINITY disables it).
+ *   softmax_scale: tau (0.125 for head_dim 64).
+ *   window:  0 = full causal; W > 0: key j is visible to query i iff
+ *            0 <= i - j < W (W = 128 counts the query itself).
+ *   out:     bf16, same layout as q, o_strides like q_strides.
+ *   workspace: device scratch of at least gptoss_attn_prefill_workspace_size()
+ *            bytes, 256-byte aligned; its content need not be initialised.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads). A row with no
+ * visible key (only possible for empty sequences) writes nothing.
+ */
+size_t gptoss_attn_prefill_workspace_size(const gptoss_seq_desc* desc);
+gptoss_status gptoss_attn_prefill(const gptoss_seq_desc* desc,
+                                  const void* q, const int64_t q_strides[3],
+                                  const void* k, const int64_t k_strides[3],
+                                  const void* v, const int64_t v_strides[3],
+                                  const float* sinks, float softmax_scale, int32_t window,
+                                  const void* table, int32_t table_rows, int32_t rotary_dim,
+                                  void* out, const int64_t o_strides[3],
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptoss_attn_prefill with an explicit choice of where k is rotated when a
+ * table is given (results are bit-identical either way):
+ *   GPTOSS_KROT_AUTO      the library's choice (fused for window layers,
+ *                         separate for full-causal layers)
+ *   GPTOSS_KROT_FUSED     k rotated while each tile is staged into LDS
+ *   GPTOSS_KROT_SEPARATE  k rotated once into the workspace, then attended
+ * Any other value returns GPTOSS_ERR_SHAPE.
+ */
+typedef enum { GPTOSS_KROT_AUTO = 0, GPTOSS_KROT_FUSED = 1, GPTOSS_KROT_SEPARATE = 2 } gptoss_k_rotation;
+gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc,
+                                     const void* q, const int64_t q_strides[3],
+                                     const void* k, const int64_t k_strides[3],
+                                     const void* v, const int64_t v_strides[3],
+                                     const float* sinks, float softmax_scale, int32_t window,
+                                     const void* table, int32_t table_rows, int32_t rotary_dim,
+                                     void* out, const int64_t o_strides[3],
+                                     void* workspace, size_t workspace_bytes, int32_t k_rotation,
+                                     void* stream);
+
+/*
+ * Decode attention: one new query token per sequence against a KV cache
+ * (the per-step attention of autoregressive generation, Transformers v4.55.0
+ *  release notes, generate(); same sink / GQA / window rules as prefill).
+ *   q:        bf16 [N, Hq, D], q_strides[2] = element strides of (seq, head);
+ *             un-rotated if a table is given (rotated at position L_n - 1).
+ *   k_cache, v_cache: bf16 [N, max_cache_len, Hkv, D]; kv_strides[3] = element
+ *             strides of (seq, position, head), shared by K and V. K rows are
+ *             stored already rotated at their own positions.
+ *   cache_seqlens: device int32 [N]; L_n counts the cached rows INCLUDING the
+ *             new token's own (already appended), 1 <= L_n <= max_cache_len.
+ *             The query sits at position L_n - 1 and sees rows 0 .. L_n - 1,
+ *             or the last min(L_n, W) of them on a window layer.
+ *   out:      bf16 [N, Hq, D], o_strides[2].
+ *   num_splits: key chunks per sequence processed in parallel and merged
+ *             (0 = choose automatically); results agree up to fp32
+ *             reassociation for any value.
+ *   workspace: >= gptoss_attn_decode_workspace_size(...) bytes.
+ */
+size_t gptoss_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t max_cache_len, int32_t num_splits);
+gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim,
+                                 const void* q, const int64_t q_strides[2],
+                                 const void* k_cache, const void* v_cache,
+                                 const int64_t kv_strides[3],
+                                 const int32_t* cache_seqlens, int32_t max_cache_len,
+                                 const float* sinks, float softmax_scale, int32_t window,
+                                 const void* table, int32_t table_rows, int32_t rotary_dim,
+                                 void* out, const int64_t o_strides[2],
+                                 void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTOSS_ATTN_H */

@@ -66,7 +66,9 @@ def yarn_params(cfg: RopeConfig):
         raise ValueError("rotary_dim must be even, positive and at most head_dim")
     half = d // 2
     idx = np.arange(half, dtype=np.float64)
-    theta = np.power(float(cfg.base), -(2.0 * idx) / d)
+    # math.pow is the C library's pow, correctly rounded; numpy's vectorised
+    # power can be one ulp away from it.
+    theta = np.array([math.pow(float(cfg.base), -(2.0 * i) / d) for i in range(half)])
     s = float(cfg.scaling_factor)
     if s <= 1.0:
         return theta, 1.0, (None, None)

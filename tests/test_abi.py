@@ -1,0 +1,184 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+computes the host-side YaRN parameters exactly like the oracle, and rejects bad
+arguments with the documented status codes before launching anything.
+
+No call here reaches a kernel launch (each returns on argument checks first).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_yarn_rope_amd import _lib
+from attention_yarn_rope_amd._lib import I64x2, I64x3, RopeConfig, SeqDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gptoss_attn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_yarn_rope_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gptoss_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gptoss_attn.h but not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.gptoss_abi_version() == 1
+    for code in range(6):
+        assert lib.gptoss_status_string(code)
+    assert lib.gptoss_status_string(99) == b"unknown status"
+
+
+def _cfg(**kw):
+    base = dict(head_dim=64, rotary_dim=64, base=150000.0, scaling_factor=32.0, initial_context_length=4096,
+                ntk_alpha=1.0, ntk_beta=32.0)
+    base.update(kw)
+    return RopeConfig(**base)
+
+
+@pytest.mark.parametrize("kw", [{}, {"scaling_factor": 1.0}, {"base": 10000.0, "scaling_factor": 4.0},
+                                {"rotary_dim": 32}])
+def test_yarn_params_match_oracle_exactly(lib, kw):
+    c = _cfg(**kw)
+    n = c.rotary_dim // 2
+    om = (ctypes.c_double * n)()
+    conc = ctypes.c_double()
+    assert lib.gptoss_yarn_params(ctypes.byref(c), om, ctypes.byref(conc)) == OK
+    ref_om, ref_c, _ = oracle.yarn_params(oracle.RopeConfig(**kw))
+    assert np.array_equal(np.array(list(om)), ref_om)
+    assert conc.value == ref_c
+
+
+def test_yarn_param_errors(lib):
+    om = (ctypes.c_double * 32)()
+    assert lib.gptoss_yarn_params(None, om, None) == ERR_NULL
+    assert lib.gptoss_yarn_params(ctypes.byref(_cfg(rotary_dim=63)), om, None) == ERR_SHAPE
+    assert lib.gptoss_yarn_params(ctypes.byref(_cfg(rotary_dim=128)), om, None) == ERR_SHAPE
+    assert lib.gptoss_yarn_params(ctypes.byref(_cfg(ntk_beta=0.5)), om, None) == ERR_SHAPE
+    assert b"ntk" in lib.gptoss_last_error()
+
+
+def test_table_init_errors(lib):
+    assert lib.gptoss_rope_table_init(ctypes.byref(_cfg()), 10, None, None) == ERR_NULL
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.gptoss_rope_table_init(ctypes.byref(_cfg()), 0, fake, None) == ERR_SHAPE
+    assert lib.gptoss_rope_table_init(ctypes.byref(_cfg(rotary_dim=7)), 10, fake, None) == ERR_SHAPE
+
+
+def _desc(**kw):
+    d = dict(layout=0, batch=2, seqlen=128, max_seqlen=128, cu_seqlens=None, num_q_heads=64, num_kv_heads=8,
+             head_dim=64)
+    d.update(kw)
+    return SeqDesc(**d)
+
+
+P = ctypes.c_void_p(0x10000)     # aligned fake device pointers: never dereferenced on these paths
+S3 = I64x3(128 * 64 * 64, 64 * 64, 64)
+K3 = I64x3(128 * 8 * 64, 8 * 64, 64)
+
+
+def _prefill(lib, desc, **kw):
+    a = dict(q=P, qs=S3, k=P, ks=K3, v=P, vs=K3, sinks=P, scale=0.125, window=0, table=P, rows=4096, rd=64,
+             out=P, os=S3, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.gptoss_attn_prefill(ctypes.byref(desc) if desc is not None else None, a["q"], a["qs"], a["k"],
+                                   a["ks"], a["v"], a["vs"], a["sinks"], a["scale"], a["window"], a["table"],
+                                   a["rows"], a["rd"], a["out"], a["os"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_argument_errors(lib):
+    d = _desc()
+    assert _prefill(lib, None) == ERR_NULL
+    assert _prefill(lib, _desc(head_dim=128)) == ERR_UNSUPPORTED
+    assert _prefill(lib, _desc(num_q_heads=60)) == ERR_UNSUPPORTED
+    assert _prefill(lib, _desc(layout=7)) == ERR_SHAPE
+    assert _prefill(lib, _desc(layout=1, batch=2, seqlen=100, max_seqlen=50)) == ERR_NULL   # no cu_seqlens
+    assert _prefill(lib, d, q=None) == ERR_NULL
+    assert _prefill(lib, d, window=-1) == ERR_SHAPE
+    assert _prefill(lib, d, scale=float("nan")) == ERR_SHAPE
+    assert _prefill(lib, d, rd=32) == ERR_UNSUPPORTED
+    assert _prefill(lib, d, rows=100) == ERR_SHAPE               # table shorter than the sequence
+    assert _prefill(lib, d, qs=I64x3(128 * 64 * 64, 64 * 64, 65)) == ERR_UNSUPPORTED   # misaligned stride
+    assert _prefill(lib, d, q=ctypes.c_void_p(0x10002)) == ERR_UNSUPPORTED             # misaligned pointer
+    assert _prefill(lib, d, wsb=16) == ERR_WORKSPACE
+    assert _prefill(lib, d, ws=None) == ERR_WORKSPACE
+    assert _prefill(lib, d, ws=ctypes.c_void_p(0x10010)) == ERR_WORKSPACE               # not 256-byte aligned
+    assert _prefill(lib, _desc(batch=0)) == OK                   # nothing to do, nothing launched
+
+
+def test_prefill_workspace_size(lib):
+    d = _desc(batch=4, seqlen=4096, max_seqlen=4096)
+    assert lib.gptoss_attn_prefill_workspace_size(ctypes.byref(d)) == 4 * 4096 * 8 * 64 * 2
+    t = _desc(layout=1, batch=16, seqlen=65171, max_seqlen=8179, cu_seqlens=P)
+    ws = lib.gptoss_attn_prefill_workspace_size(ctypes.byref(t))
+    assert ws >= 65171 * 8 * 64 * 2 + ((65171 + 31) // 32 + 16) * 8
+    assert lib.gptoss_attn_prefill_workspace_size(ctypes.byref(_desc(head_dim=80))) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(n=4, hq=64, hkv=8, d=64, q=P, qs=I64x2(64 * 64, 64), k=P, v=P, kvs=I64x3(1024 * 8 * 64, 8 * 64, 64),
+             lens=P, lmax=1024, sinks=P, scale=0.125, window=0, table=P, rows=1024, rd=64, out=P,
+             os=I64x2(64 * 64, 64), ws=P, wsb=1 << 30, splits=0)
+    a.update(kw)
+    return lib.gptoss_attn_decode(a["n"], a["hq"], a["hkv"], a["d"], a["q"], a["qs"], a["k"], a["v"], a["kvs"],
+                                  a["lens"], a["lmax"], a["sinks"], a["scale"], a["window"], a["table"], a["rows"],
+                                  a["rd"], a["out"], a["os"], a["ws"], a["wsb"], a["splits"], None)
+
+
+def test_decode_argument_errors(lib):
+    assert _decode(lib, d=128) == ERR_UNSUPPORTED
+    assert _decode(lib, hq=32) == ERR_UNSUPPORTED
+    assert _decode(lib, lmax=0) == ERR_SHAPE
+    assert _decode(lib, splits=-1) == ERR_SHAPE
+    assert _decode(lib, window=-5) == ERR_SHAPE
+    assert _decode(lib, lens=None) == ERR_NULL
+    assert _decode(lib, rows=1000) == ERR_SHAPE
+    assert _decode(lib, wsb=8) == ERR_WORKSPACE
+    assert _decode(lib, kvs=I64x3(1024 * 8 * 64, 8 * 64, 63)) == ERR_UNSUPPORTED
+    assert _decode(lib, n=0) == OK
+
+
+def test_decode_workspace_size(lib):
+    # 64 sequences x 64 heads x ceil(32768 / 512) splits x (64 + 2) floats
+    ws = lib.gptoss_attn_decode_workspace_size(64, 64, 32768, 0)
+    assert ws == 64 * 64 * 64 * 64 * 4 + 64 * 64 * 64 * 2 * 4
+    assert lib.gptoss_attn_decode_workspace_size(2, 64, 1000, 3) >= 2 * 64 * 3 * 66 * 4
+    assert lib.gptoss_attn_decode_workspace_size(2, 64, 0, 0) == 0
+
+
+def test_rope_qk_argument_errors(lib):
+    d = _desc()
+    f = lib.gptoss_rope_qk
+    assert f(ctypes.byref(d), P, S3, P, K3, P, P, None, 4096, 64, None) == ERR_NULL
+    assert f(ctypes.byref(d), P, S3, P, K3, P, P, P, 10, 64, None) == ERR_SHAPE
+    assert f(ctypes.byref(_desc(head_dim=32)), P, S3, P, K3, P, P, P, 4096, 64, None) == ERR_UNSUPPORTED
+    assert f(ctypes.byref(_desc(seqlen=0)), P, S3, P, K3, P, P, P, 4096, 64, None) == OK
+
+
+def test_prefill_ex_rejects_unknown_k_rotation(lib):
+    d = _desc()
+    st = lib.gptoss_attn_prefill_ex(ctypes.byref(d), P, S3, P, K3, P, K3, P, 0.125, 0, P, 4096, 64, P, S3, P,
+                                    1 << 30, 9, None)
+    assert st == ERR_SHAPE

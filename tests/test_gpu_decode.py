@@ -1,0 +1,82 @@
+"""GPU parity of the split-KV decode kernels against the fp64 oracle (through the C ABI).
+
+Also: decode equals the last row of prefill on the same data (the cache holds
+rope_qk's rotated k), results do not depend on the split count beyond fp32
+reassociation, and sequences of length 1 and sinks of -inf behave.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_yarn_rope_amd as gx
+import oracle
+from attention_yarn_rope_amd import workloads as wl
+from helpers import assert_close, np64, say
+
+pytestmark = pytest.mark.gpu
+CFG = oracle.RopeConfig()
+TAU = 0.125
+
+
+@pytest.fixture(scope="module")
+def table():
+    return gx.rope_table(40000)
+
+
+def _ref(inp, window, rows=None):
+    rows = range(len(inp.lengths)) if rows is None else rows
+    idx = list(rows)
+    return oracle.decode(np64(inp.q[idx]), np64(inp.k_cache[idx]), np64(inp.v_cache[idx]),
+                         [inp.lengths[i] for i in idx], np64(inp.sinks), TAU, window, CFG)
+
+
+def _run(inp, window, table, num_splits=0):
+    return gx.attn_decode(inp.q.cuda(), inp.k_cache.cuda(), inp.v_cache.cuda(), inp.cache_seqlens.cuda(),
+                          inp.sinks.cuda(), window=window, table=table, num_splits=num_splits)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_decode_ragged(table, window):
+    inp = wl.decode(0, 0, 0, seed=21, max_len=2100, lengths=[1, 2, 127, 128, 129, 511, 512, 513, 2000, 2100])
+    say(f"[gpu] decode ragged window={window}")
+    assert_close(_run(inp, window, table), _ref(inp, window), f"decode W={window}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_decode_split_counts(table, splits):
+    inp = wl.decode(0, 0, 0, seed=22, max_len=3000, lengths=[3000, 1700, 900])
+    say(f"[gpu] decode num_splits={splits}")
+    out = _run(inp, 0, table, num_splits=splits)
+    auto = _run(inp, 0, table)
+    assert_close(out, _ref(inp, 0), f"decode splits={splits}")
+    assert (np64(out) - np64(auto)).__abs__().max() <= 2 ** -6
+
+
+def test_decode_equals_last_prefill_row(table):
+    """Cache k = rope_qk(k); decode's q is the raw q of the last token."""
+    B, S = 2, 777
+    inp = wl.prefill_bshd(B, S, seed=23)
+    q, k, v, s = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda()
+    say("[gpu] decode == last prefill row")
+    for window in (0, 128):
+        pre = gx.attn_prefill(q, k, v, s, window=window, table=table)
+        _, kr = gx.rope_qk(q, k, table)
+        lens = torch.full((B,), S, dtype=torch.int32, device="cuda")
+        dec = gx.attn_decode(q[:, S - 1].contiguous(), kr, v, lens, s, window=window, table=table)
+        # different blockings of the same sums: fp32 reassociation plus one bf16 rounding apart
+        assert_close(dec, np64(pre[:, S - 1]), f"decode vs prefill W={window}", atol=4e-3, rtol=1e-2)
+
+
+def test_decode_sink_minus_inf_and_hkv2(table):
+    inp = wl.decode(0, 0, 0, seed=24, max_len=700, lengths=[700, 1, 300], hq=16, hkv=2)
+    inp.sinks = torch.full((16,), -float("inf"))
+    say("[gpu] decode sink -inf, Hkv=2")
+    for w in (0, 128):
+        assert_close(_run(inp, w, table), _ref(inp, w), f"decode -inf W={w}")
+
+
+def test_decode_deterministic(table):
+    inp = wl.decode(0, 0, 0, seed=25, max_len=5000, lengths=[5000, 4000])
+    a, b = _run(inp, 0, table), _run(inp, 0, table)
+    assert torch.equal(a, b)
