@@ -53,10 +53,14 @@ def yarn_params(cfg=None):
     return list(om), c.value
 
 
-def rope_table(num_positions, cfg=None, device="cuda"):
+def rope_table(num_positions, cfg=None, device="cuda", out=None):
     """bf16 [num_positions, rotary_dim] table: cos half then sin half, concentration applied."""
     cfg = cfg or rope_config()
-    t = torch.empty((num_positions, cfg.rotary_dim), dtype=torch.bfloat16, device=device)
+    t = out if out is not None else torch.empty((num_positions, cfg.rotary_dim), dtype=torch.bfloat16,
+                                                device=device)
+    _bf16(t, "table")
+    if tuple(t.shape) != (num_positions, cfg.rotary_dim) or not t.is_contiguous():
+        raise ValueError("out must be a contiguous [num_positions, rotary_dim] tensor")
     check("gptoss_rope_table_init",
           _lib.load().gptoss_rope_table_init(ctypes.byref(cfg), num_positions, _ptr(t), _stream()))
     return t

@@ -128,6 +128,15 @@ __device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* lds_ptr) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Sum of the two bf16 halves of w, added to acc (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, acc, false);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(bf16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

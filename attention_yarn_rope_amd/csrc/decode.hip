@@ -31,8 +31,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   __shared__ float red_l[4][8];
   __shared__ float red_o[4][8][kHeadDim];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
+  const int g = blockIdx.x;       // KV heads fastest: the 8 groups reading the same cache rows run together
+  const int split = blockIdx.y;
   const int n = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -74,9 +74,11 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = w0; s0 < w0 + per_wave; s0 += SUB) {
-    // K: A operand rows = keys s0 + kb*16 + col, k = d
-    bf16x8_t ka[2][2];
+  // K (A operand: rows = keys, k = d) and V rows for the 32 keys at s0; rows
+  // at or beyond c1 read as zero
+  bf16x8_t ka[2][2];
+  uint4 vr[4];
+  auto load_block = [&](int s0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = s0 + kb * 16 + col;
@@ -89,21 +91,26 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
       ka[kb][0] = as_bf16x8(a0);
       ka[kb][1] = as_bf16x8(a1);
     }
-    // V rows s0 .. s0+31 into this wave's LDS block: lane -> rows (lane>>3) + 8i, 16 B chunk lane&7
-    uint4 vr[4];
+    // V rows s0 .. s0+31: lane -> rows (lane>>3) + 8i, 16 B chunk lane&7
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = (lane >> 3) + 8 * i;
-      const int key = s0 + row;
+      const int key = s0 + (lane >> 3) + 8 * i;
       vr[i] = make_uint4(0, 0, 0, 0);
       if (key < c1) vr[i] = ldg16(vbase + (int64_t)key * p.kv_sp + 8 * (lane & 7));
     }
+  };
+  const int w1 = min(w0 + per_wave, c1);   // this wave's keys: [w0, w1)
+  if (w0 < w1) load_block(w0);
+  for (int s0 = w0; s0 < w1; s0 += SUB) {
+    const bf16x8_t k00 = ka[0][0], k01 = ka[0][1], k10 = ka[1][0], k11 = ka[1][1];
+    const uint4 v0 = vr[0], v1 = vr[1], v2 = vr[2], v3 = vr[3];
+    if (s0 + SUB < w1) load_block(s0 + SUB);   // next block in flight during this one
     f32x4_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-      z = mfma16(ka[kb][0], qf[0], z);
-      sacc[kb] = mfma16(ka[kb][1], qf[1], z);
+      z = mfma16(kb ? k10 : k00, qf[0], z);
+      sacc[kb] = mfma16(kb ? k11 : k01, qf[1], z);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -131,16 +138,17 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
       w[2 * kb + 1] = pack_bf16x2(e2, e3);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) psum += bf16_lo(w[i]) + bf16_hi(w[i]);
+    for (int i = 0; i < 4; ++i) psum = add_bf16x2(w[i], psum);
     lsum = lsum * f + psum;
     m = mnew;
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] *= f;
     const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 8 * i) * DVS + 8 * (lane & 7)) = vr[i];
+    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 0) * DVS + 8 * (lane & 7)) = v0;
+    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 8) * DVS + 8 * (lane & 7)) = v1;
+    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 16) * DVS + 8 * (lane & 7)) = v2;
+    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 24) * DVS + 8 * (lane & 7)) = v3;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -189,7 +197,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   if ((tid & 31) == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(M, lt);
 }
 
-// One wave per (sequence, query head); lane = head dim.
+// One wave per (sequence, query head). Splits across lanes for the max and the
+// weights, then lane = head dim for the weighted sum of the partial outputs.
 __global__ __launch_bounds__(NT) void decode_combine_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
@@ -202,19 +211,37 @@ __global__ __launch_bounds__(NT) void decode_combine_kernel(DecodeParams p) {
   const int lo = (p.window > 0) ? max(0, L - p.window) : 0;
   const int nsplit = min((L - lo + p.chunk - 1) / p.chunk, p.num_splits);
   const float sig = __ldg(p.sinks + h) * kLog2e;
-  float M = sig;
   const int64_t base = ((int64_t)n * p.num_kv_heads + g) * p.num_splits;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.part_ml[((base + s) * kGroup + c) * 2]);
-  const float Mu = (M == -INFINITY) ? 0.0f : M;
-  float l = __builtin_amdgcn_exp2f(sig - Mu);
-  float o = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t slot = (base + s) * kGroup + c;
-    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
-    const float f = __builtin_amdgcn_exp2f(ml.x - Mu);
-    l += ml.y * f;
-    o += p.part_o[slot * kHeadDim + lane] * f;
+  float M = sig;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < nsplit) M = fmaxf(M, p.part_ml[((base + s) * kGroup + c) * 2]);
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float Mu = (M == -INFINITY) ? 0.0f : M;
+  float l = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int s = s0 + lane;
+    float wgt = 0.0f;
+    if (s < nsplit) {
+      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + ((base + s) * kGroup + c) * 2);
+      wgt = __builtin_amdgcn_exp2f(ml.x - Mu);
+      l += ml.y * wgt;
+    }
+    const int cnt = min(64, nsplit - s0);
+    const float* po = p.part_o + ((base + s0) * kGroup + c) * kHeadDim + lane;
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {
+      const float a0 = po[(int64_t)(j + 0) * kGroup * kHeadDim], a1 = po[(int64_t)(j + 1) * kGroup * kHeadDim];
+      const float a2 = po[(int64_t)(j + 2) * kGroup * kHeadDim], a3 = po[(int64_t)(j + 3) * kGroup * kHeadDim];
+      o += a0 * __shfl(wgt, j) + a1 * __shfl(wgt, j + 1) + a2 * __shfl(wgt, j + 2) + a3 * __shfl(wgt, j + 3);
+    }
+    for (; j < cnt; ++j) o += po[(int64_t)j * kGroup * kHeadDim] * __shfl(wgt, j);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  l += __builtin_amdgcn_exp2f(sig - Mu);
   const float r = (l > 0.0f) ? o / l : 0.0f;
   // two lanes per bf16 pair: even lane stores the pair
   const float r_next = __shfl_down(r, 1);
@@ -228,7 +255,7 @@ __global__ __launch_bounds__(NT) void decode_combine_kernel(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
-  dim3 grid(p.num_splits, p.num_kv_heads, p.num_seqs);
+  dim3 grid(p.num_kv_heads, p.num_splits, p.num_seqs);
   if (p.table)
     hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(NT), 0, stream, p);
   else

@@ -20,12 +20,12 @@
 // needs (keys permuted consistently between V^T and P^T). V^T comes straight
 // from the row-major V tile in LDS through ds_read_b64_tr_b16.
 //
-// Online softmax in log2 units, seeded with the sink: m = sigma_h*log2(e),
-// l = 1. The running reference m is only raised when a tile's maximum exceeds
-// it by more than 8 (p stays <= 2^8, safe in fp32 and bf16), which skips the
-// rescale of the accumulator on almost every tile; the result is the same
-// ratio. Tiles fully visible to every query of the item skip the mask; tiles
-// fully hidden are never visited.
+// Softmax in log2 units against a per-row reference seeded with the sink
+// logit (the sink term exp(sigma - ref) = 1 starts the row sum); the reference
+// only moves in a rare fallback (a tile's partial row sum beyond 2^100), so
+// the hot loop has no running max and no accumulator rescale. Tiles fully
+// visible to every query of the item skip the mask; tiles fully hidden are
+// never visited.
 #include "common.h"
 #include "internal.h"
 
@@ -37,7 +37,8 @@ constexpr int NK = 64;          // keys per KV tile
 constexpr int NT = 256;         // threads per work group (4 waves)
 constexpr int KS = 72;          // LDS row stride of the K tile (144 B): conflict-free 16 B reads
 constexpr int VS = 80;          // LDS row stride of the V tile (160 B): conflict-free tr16 reads
-constexpr float kRescaleGap = 8.0f;
+constexpr float kSumLimit = 0x1p100f;   // bound of a tile's partial row sum before the reference moves
+constexpr float kRaiseGap = 8.0f;       // the reference moves to a new max more than this far above it
 
 __device__ __forceinline__ float wave_xor_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
@@ -103,7 +104,7 @@ void prefill_kernel(PrefillParams p) {
   int qpos[2];
   qpos[0] = q0 + col;
   qpos[1] = q0 + 16 + col;
-  float m[4], lsum[4];
+  float ref[4], lsum[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int head = g * kGroup + wave * 2 + (cb >> 1);
@@ -121,9 +122,12 @@ void prefill_kernel(PrefillParams p) {
     }
     qf[cb][0] = as_bf16x8(y1);
     qf[cb][1] = as_bf16x8(y2);
-    const float sink = __ldg(p.sinks + head);
-    m[cb] = sink * kLog2e;              // -inf stays -inf
-    lsum[cb] = (grp == 0) ? 1.0f : 0.0f;  // the sink's exp(sigma - m) = 1, counted once
+    // reference = the sink logit (log2 units); the sink term exp2(sigma - ref) = 1
+    // is counted once, in lane group 0. A sink of -inf contributes 0 (reference 0).
+    const float sink = __ldg(p.sinks + head) * kLog2e;
+    const bool has_sink = sink > -INFINITY;
+    ref[cb] = has_sink ? sink : 0.0f;
+    lsum[cb] = (grp == 0 && has_sink) ? 1.0f : 0.0f;
   }
 
   f32x4_t oacc[4][4];  // [d block][column block]
@@ -211,56 +215,61 @@ void prefill_kernel(PrefillParams p) {
         }
     }
 
-    // ---- online softmax (log2 units), lazy rescale ----
-    float mx[4];
-    bool need = false;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      float v = sacc[0][cb][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v = fmaxf(v, sacc[kb][cb][r]);
-      mx[cb] = v * sl;
-      need |= mx[cb] > m[cb] + kRescaleGap;
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const float mt = wave_xor_max(mx[cb]);
-        if (mt > m[cb] + kRescaleGap) {   // uniform across the 4 lanes of the column
-          const float f = __builtin_amdgcn_exp2f(m[cb] - mt);   // m = -inf -> 0
-          lsum[cb] *= f;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) oacc[db][cb] *= f;
-          m[cb] = mt;
-        }
-      }
-    }
-
+    // ---- online softmax against a fixed reference (log2 units) ----
+    // p = exp2(s*tau*log2(e) - ref). The reference starts at the sink logit and
+    // only moves when a tile's bf16 row sum leaves [0, 2^100] (a score that far
+    // above the reference, or an overflow): then the tile's true column max
+    // becomes the reference, l and O are rescaled and the tile is redone. Values
+    // below or above the reference by up to 2^100 lose no relative precision in
+    // fp32 / bf16, so the result is the same ratio as with a running max.
     bf16x8_t pf[4][2];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const float mu = (m[cb] == -INFINITY) ? 0.0f : m[cb];
+    float tsum[4];
+    bool bad = false;
+    auto exp_tile = [&](int cb) {
       uint32_t w[8];
+      const float nr = -ref[cb];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][0], sl, -mu));
-        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][1], sl, -mu));
-        float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][2], sl, -mu));
-        float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][3], sl, -mu));
-        w[2 * kb] = pack_bf16x2(e0, e1);
-        w[2 * kb + 1] = pack_bf16x2(e2, e3);
+        w[2 * kb] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][0], sl, nr)),
+                                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][1], sl, nr)));
+        w[2 * kb + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][2], sl, nr)),
+                                    __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][3], sl, nr)));
       }
       // row sum of the bf16-rounded probabilities actually used by PV
-      float s = lsum[cb];
+      float ts = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += bf16_lo(w[i]) + bf16_hi(w[i]);
-      lsum[cb] = s;
+      for (int i = 0; i < 8; ++i) ts = add_bf16x2(w[i], ts);
+      tsum[cb] = ts;
       // keys pi(grp, e): e < 4 -> 4*grp + e of key block 2ks, e >= 4 -> of key block 2ks+1
       pf[cb][0] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       pf[cb][1] = __builtin_bit_cast(bf16x8_t, make_uint4(w[4], w[5], w[6], w[7]));
+    };
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      exp_tile(cb);
+      bad |= !(tsum[cb] <= kSumLimit);
     }
+    if (__any(bad)) {   // rare, wave-uniform
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v = __builtin_fmaxf(v, sacc[kb][cb][r]);
+        const float mt = wave_xor_max(v) * sl;     // the column's max (log2 units)
+        if (mt > ref[cb] + kRaiseGap) {            // uniform across the 4 lanes of the column
+          const float f = __builtin_amdgcn_exp2f(ref[cb] - mt);
+          lsum[cb] *= f;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) oacc[db][cb] *= f;
+          ref[cb] = mt;
+        }
+        exp_tile(cb);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) lsum[cb] += tsum[cb];
 
     // ---- O^T += V^T P^T ----
 #pragma unroll

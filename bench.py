@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the GPT-OSS attention hot path on one MI355X.
+
+Step = one pass of the prefill hot path over the dense BSHD workload
+(B=4, S=4096, 64 query / 8 KV heads of width 64, bf16 N(0,1) inputs, fp32
+N(0,1) sinks): build the YaRN cos/sin table for the 4096 positions, then one
+full-causal layer and one sliding-window-128 layer, each with q and k rotated
+inside the attention call. `value` is unmasked prefill TFLOP/s over the step
+(4 * D * Hq FLOPs per visible (query, key) pair). The decode half of the metric
+(64 sequences, cache lengths uniform in [1024, 32768], full and window-128
+layers) is timed in the same run and reported under "decode".
+
+Timing uses HIP events recorded on the stream the library launches on, around
+every call inside the timed region; the whole region is bracketed by device
+synchronisation. The CPU baseline is the fp64 oracle on a time-bounded sample
+of query rows of the same workload, on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --profile {prefill-full,prefill-window,decode-full,copy} --steps K
+       (the --profile modes run only the named call, for rocprofv3)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (%MFMA peak) + decode KV GB/s (%HBM peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+WINDOW = 128
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["attention_yarn_rope_amd/csrc/prefill.hip", "attention_yarn_rope_amd/csrc/common.h",
+                  "attention_yarn_rope_amd/csrc/decode.hip"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(name, launches_bytes_unit=1):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    profiles/<name>.counters.json holds FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) for the kernel, the same counters for a plain copy kernel of known
+    size (the calibration factor), and the hash of the kernel sources at the
+    time; a changed kernel makes the figure stale (None).
+    """
+    path = os.path.join(PROFILES, f"{name}.counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_hash") != source_hash(KERNEL_SOURCES):
+        return None
+    return c["traffic_bytes_per_launch"]
+
+
+def ensure_built():
+    from attention_yarn_rope_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_yarn_rope_amd import build
+        build.build(verbose=False)
+
+
+class Timer:
+    """Per-call HIP event pairs on the current (library) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        stream = self.torch.cuda.current_stream()
+        s.record(stream)
+        fn()
+        e.record(stream)
+        self.pairs.setdefault(name, []).append((s, e))
+
+    def mean_ms(self, name):
+        v = [s.elapsed_time(e) for s, e in self.pairs.get(name, [])]
+        return sum(v) / len(v) if v else float("nan")
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle, as it stands, on seeded query rows of the dense workload (batch 0)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    S = inp.q.shape[1]
+    q = inp.q[0].double().numpy()
+    k = inp.k[0].double().numpy()
+    v = inp.v[0].double().numpy()
+    sinks = inp.sinks.double().numpy()
+    rng = np.random.default_rng(2024)
+    order = rng.permutation(S)
+    flops, rows_done, t0 = 0, 0, time.perf_counter()
+    chunk = 32
+    while time.perf_counter() - t0 < budget_s and rows_done < S:
+        rows = np.sort(order[rows_done:rows_done + chunk])
+        for w in (0, WINDOW):
+            oracle.prefill_rows(q, k, v, sinks, 0.125, w, rows)
+            flops += sum(4 * 64 * 64 * (min(int(r) + 1, w) if w else int(r) + 1) for r in rows)
+        rows_done += len(rows)
+    secs = time.perf_counter() - t0
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(secs, 2),
+            "sample": f"{rows_done} seeded query rows x 64 heads of batch 0 of the dense B=4 S=4096 workload, "
+                      f"full-causal and window-128 layers, fp64 numpy on the host CPU"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--k-rotation", default="auto", choices=["auto", "fused", "separate"])
+    ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy"])
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): this attention path has no "
+              "multi-GPU mode; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    ensure_built()
+    import torch
+    import attention_yarn_rope_amd as gx
+    from attention_yarn_rope_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.profile == "copy":
+        # calibration for the HBM counters: a plain 1 GiB device-to-device copy
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {args.steps} x 1 GiB")
+        return
+
+    # ---------------- prefill (the step) ----------------
+    log("[bench] generating dense B=4 S=4096 workload")
+    inp = wl.dense()
+    q, k, v, sinks = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.sinks))
+    S = q.shape[1]
+    table = torch.empty((S, 64), dtype=torch.bfloat16, device=dev)
+    o_full = torch.empty_like(q)
+    o_win = torch.empty_like(q)
+    ws = torch.empty(max(gx.prefill_workspace_size(q, k), 1), dtype=torch.uint8, device=dev)
+    gx.rope_table(S, out=table)
+
+    def call_full():
+        gx.attn_prefill(q, k, v, sinks, window=0, table=table, out=o_full, workspace=ws, k_rotation=args.k_rotation)
+
+    def call_win():
+        gx.attn_prefill(q, k, v, sinks, window=WINDOW, table=table, out=o_win, workspace=ws,
+                        k_rotation=args.k_rotation)
+
+    if args.profile in ("prefill-full", "prefill-window"):
+        fn = call_full if args.profile == "prefill-full" else call_win
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"{args.profile}: {args.steps} launches")
+        return
+
+    lengths = [S] * q.shape[0]
+    flops_full = wl.prefill_flops(lengths, 0)
+    flops_win = wl.prefill_flops(lengths, WINDOW)
+    bytes_prefill = wl.prefill_bytes(q.shape[0] * S, S)
+
+    if args.profile is None:
+        timer = Timer(torch)
+        for _ in range(args.warmup):
+            gx.rope_table(S, out=table)
+            call_full()
+            call_win()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            timer.run("table", lambda: gx.rope_table(S, out=table))
+            timer.run("full", call_full)
+            timer.run("window", call_win)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_step = wall * 1e3 / args.steps
+        ms_full, ms_win, ms_table = timer.mean_ms("full"), timer.mean_ms("window"), timer.mean_ms("table")
+        log(f"[bench] prefill step {ms_step:.3f} ms (full {ms_full:.3f} ms, window {ms_win:.3f} ms, "
+            f"table {ms_table:.4f} ms)")
+        del timer
+
+    # ---------------- decode ----------------
+    decode_obj = None
+    if not args.no_decode or args.profile == "decode-full":
+        log("[bench] generating decode workload: 64 sequences, lengths uniform in [1024, 32768]")
+        dinp = wl.decode64()
+        dq = dinp.q.to(dev)
+        kc = dinp.k_cache.to(dev)
+        vc = dinp.v_cache.to(dev)
+        lens = dinp.cache_seqlens.to(dev)
+        dsinks = dinp.sinks.to(dev)
+        del dinp.k_cache, dinp.v_cache
+        dtable = gx.rope_table(kc.shape[1])
+        d_out = torch.empty_like(dq)
+        dws = torch.empty(gx.decode_workspace_size(dq.shape[0], 64, kc.shape[1]), dtype=torch.uint8, device=dev)
+
+        def dec(w):
+            return lambda: gx.attn_decode(dq, kc, vc, lens, dsinks, window=w, table=dtable, out=d_out,
+                                          workspace=dws)
+
+        if args.profile == "decode-full":
+            for _ in range(args.steps):
+                dec(0)()
+            torch.cuda.synchronize()
+            log(f"decode-full: {args.steps} launches")
+            return
+        timer = Timer(torch)
+        for _ in range(args.warmup):
+            dec(0)()
+            dec(WINDOW)()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            timer.run("dfull", dec(0))
+            timer.run("dwin", dec(WINDOW))
+        torch.cuda.synchronize()
+        ms_df, ms_dw = timer.mean_ms("dfull"), timer.mean_ms("dwin")
+        b_full = wl.decode_bytes(dinp.lengths, 0)
+        b_win = wl.decode_bytes(dinp.lengths, WINDOW)
+        gbs = b_full / (ms_df * 1e-3) / 1e9
+        decode_obj = {
+            "workload": "decode: 64 sequences x 1 token, cache lengths uniform in [1024, 32768] "
+                        f"(sum {sum(dinp.lengths)}), Hq=64 Hkv=8 D=64, bf16 cache",
+            "value": round(gbs, 1), "unit": "GB/s", "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "ms_full_layer": round(ms_df, 4), "ms_window_layer": round(ms_dw, 4),
+            "bytes_full_layer": b_full, "bytes_window_layer": b_win,
+            "window_layer_GBps": round(b_win / (ms_dw * 1e-3) / 1e9, 1),
+            "traffic": counters_traffic("decode_split_full_64seq"),
+        }
+        log(f"[bench] decode full {ms_df:.3f} ms = {gbs:.0f} GB/s; window {ms_dw:.4f} ms")
+        del kc, vc
+
+    tflops = (flops_full + flops_win) / (ms_step * 1e-3) / 1e12
+    achieved = flops_full / (ms_full * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense BSHD prefill B=4 S=4096 Hq=64 Hkv=8 D=64: YaRN table + full-causal layer + "
+                        "window-128 layer, q/k rotated inside attention",
+            "global_batch": q.shape[0], "seq_len": S, "parallelism": "none (1 GPU)",
+            "k_rotation": args.k_rotation,
+        },
+        "roofline": {
+            "kernel": "prefill full-causal layer (gptoss_attn_prefill, window=0)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": counters_traffic("prefill_full_dense_B4_S4096"),
+            "flops_per_launch": flops_full,
+            "ms_per_launch": round(ms_full, 4),
+        },
+        "layers": {
+            "full": {"ms": round(ms_full, 4), "TFLOP/s": round(achieved, 2), "flops": flops_full},
+            "window128": {"ms": round(ms_win, 4), "TFLOP/s": round(flops_win / (ms_win * 1e-3) / 1e12, 2),
+                          "GB/s": round(bytes_prefill / (ms_win * 1e-3) / 1e9, 1),
+                          "frac_hbm_peak": round(bytes_prefill / (ms_win * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "flops": flops_win, "bytes": bytes_prefill},
+            "table_ms": round(ms_table, 5),
+        },
+        "decode": decode_obj,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline, ~{args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,101 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+The GPU computes every output; the oracle recomputes seeded samples of them one
+row (query token, all heads) at a time:
+  * dense BSHD prefill B=4, S=4096, full-causal and window-128;
+  * packed THD prefill, 16 sequences with lengths uniform in [128, 8192];
+  * long-context prefill B=1, S=131072 (row sample includes 0, 1, 127, 128, 131071);
+  * decode, 64 sequences with cache lengths uniform in [1024, 32768] (all rows).
+Tolerance as in helpers.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_yarn_rope_amd as gx
+import oracle
+from attention_yarn_rope_amd import workloads as wl
+from helpers import assert_close, np64, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+TAU = 0.125
+
+
+def _rows(S, n, seed, must=()):
+    rng = np.random.default_rng(seed)
+    r = set(int(x) for x in must if 0 <= x < S)
+    r.update(int(x) for x in rng.choice(S, size=min(n, S), replace=False))
+    return np.array(sorted(r))
+
+
+class _Rows:
+    """Indexable view of a CPU bf16 tensor that converts only the requested rows to fp64."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        return np64(self.t[torch.as_tensor(np.asarray(idx))])
+
+
+def _check_rows(out, q, k, v, sinks, window, rows, what, positions=None):
+    """out/q/k/v: one sequence ([S, H, D] tensors on CPU); rows: indices into it."""
+    ref = oracle.prefill_rows(_Rows(q), _Rows(k), _Rows(v), np64(sinks), TAU, window, rows, positions=positions)
+    assert_close(out[rows], ref, what)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_dense_bshd(window):
+    say(f"[gpu] dense B=4 S=4096 window={window}")
+    inp = wl.dense()
+    table = gx.rope_table(4096)
+    out = gx.attn_prefill(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), window=window,
+                          table=table).cpu()
+    for b in range(4):
+        rows = _rows(4096, 12, 100 + b, must=(0, 31, 32, 63, 64, 127, 128, 4095) if b == 0 else ())
+        _check_rows(out[b], inp.q[b], inp.k[b], inp.v[b], inp.sinks, window, rows, f"dense b={b} W={window}")
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_thd_16_sequences(window):
+    say(f"[gpu] THD 16 sequences window={window}")
+    inp = wl.thd()
+    assert inp.q.shape[0] == sum(inp.lengths)
+    table = gx.rope_table(8192)
+    out = gx.attn_prefill(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), window=window, table=table,
+                          cu_seqlens=inp.cu_seqlens.cuda(), max_seqlen=inp.max_seqlen).cpu()
+    cu = inp.cu_seqlens.tolist()
+    for n, L in enumerate(inp.lengths):
+        a, b = cu[n], cu[n + 1]
+        rows = _rows(L, 3, 200 + n, must=(0, L - 1))
+        _check_rows(out[a:b], inp.q[a:b], inp.k[a:b], inp.v[a:b], inp.sinks, window, rows,
+                    f"thd seq {n} (L={L}) W={window}")
+
+
+def test_long_context():
+    say("[gpu] long S=131072")
+    inp = wl.long_context()
+    table = gx.rope_table(131072)
+    q, k, v, s = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda()
+    for window, n_rows in ((128, 128), (0, 40)):
+        say(f"  window={window}")
+        out = gx.attn_prefill(q, k, v, s, window=window, table=table)[0].cpu()
+        rows = _rows(131072, n_rows, 300 + window, must=(0, 1, 127, 128, 131071))
+        _check_rows(out, inp.q[0], inp.k[0], inp.v[0], inp.sinks, window, rows, f"long W={window}")
+        del out
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_decode_64_sequences(window):
+    say(f"[gpu] decode 64 sequences window={window}")
+    inp = wl.decode64()
+    table = gx.rope_table(32768)
+    out = gx.attn_decode(inp.q.cuda(), inp.k_cache.cuda(), inp.v_cache.cuda(), inp.cache_seqlens.cuda(),
+                         inp.sinks.cuda(), window=window, table=table).cpu()
+    ref = np.zeros((64, 64, 64))
+    for n, L in enumerate(inp.lengths):
+        ref[n] = oracle.decode(np64(inp.q[n:n + 1]), np64(inp.k_cache[n:n + 1, :L]), np64(inp.v_cache[n:n + 1, :L]),
+                               [L], np64(inp.sinks), TAU, window)[0]
+    assert_close(out, ref, f"decode64 W={window}")
