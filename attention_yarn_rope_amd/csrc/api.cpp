@@ -333,18 +333,18 @@ gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc, const void* q,
                       table_rows, rotary_dim, out, o_strides, workspace, workspace_bytes, krot, stream);
 }
 
-// Keys per split: a multiple of 128 (4 waves x 32-key steps). Automatic: up to
-// 1024 keys per work group, which still gives thousands of work groups for
-// long caches while keeping the partials few.
+// Keys per split (per KV head): a multiple of 128. Automatic: up to 512 keys,
+// which gives thousands of work groups for long caches while the partials stay
+// under 2% of the cache traffic.
 static int32_t decode_chunk(int32_t eff_len, int32_t num_splits) {
-  int32_t c = num_splits > 0 ? (eff_len + num_splits - 1) / num_splits : (eff_len < 1024 ? eff_len : 1024);
+  int32_t c = num_splits > 0 ? (eff_len + num_splits - 1) / num_splits : (eff_len < 512 ? eff_len : 512);
   c = (c + 127) / 128 * 128;
   return c < 128 ? 128 : c;
 }
 
 // Upper bound of the splits any call with these sizes uses (window layers use fewer).
 static int64_t decode_split_cap(int32_t max_cache_len, int32_t num_splits) {
-  return num_splits > 0 ? num_splits : (max_cache_len + 1023) / 1024;
+  return num_splits > 0 ? num_splits : (max_cache_len + 511) / 512;
 }
 
 size_t gptoss_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_cache_len,

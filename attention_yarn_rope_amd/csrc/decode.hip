@@ -4,13 +4,16 @@
 // "nemo_automodel.components.models.gpt_oss.layers", GptOssAttention;
 // Transformers v4.55.0 release notes, "Architecture").
 //
-// Split kernel: one work group per (key chunk, KV head, sequence). The 8 query
-// heads of the KV head's group share every K/V row, which is streamed from HBM
-// exactly once: K goes straight from global memory into the MFMA A operand
-// (16 B per lane), V is staged through LDS and read transposed with
-// ds_read_b64_tr_b16. Each wave covers a quarter of the chunk in blocks of 32
-// keys with an exact online softmax; the 4 waves merge in LDS and write one
-// unnormalised partial (m, l, acc[64]) per query head.
+// Split kernel: one work group per (key chunk, sequence, group of 8 KV heads);
+// wave w takes KV head w, so the group streams whole 1 KB cache rows (8 heads
+// x 128 B) and each K/V row of a head is read from HBM exactly once for the 8
+// query heads that share it. Rows are fetched in full 128 B lines with
+// non-temporal loads (read-once data), 32 keys per step, the next step's loads
+// in flight while the current one computes. K and V pass through one per-wave
+// LDS block: K is read back as MFMA A fragments for S^T = K Q^T
+// (v_mfma_f32_16x16x32_bf16, 8 heads padded to 16 columns), V transposed with
+// ds_read_b64_tr_b16 for O^T = V^T P^T. Exact online softmax per step; each
+// wave writes one unnormalised partial (m, l, acc[64]) per query head.
 // Combine kernel: per (sequence, query head) it merges the partials and adds
 // the sink exactly once: M = max(sigma, m_s), l = exp(sigma - M) + sum l_s
 // exp(m_s - M), o = sum acc_s exp(m_s - M) / l (all in log2 units).
@@ -20,22 +23,43 @@
 namespace gptoss {
 namespace {
 
-constexpr int NT = 256;
-constexpr int SUB = 32;     // keys per wave step
-constexpr int DVS = 80;     // LDS row stride of a wave's V block (160 B)
+constexpr int NW = 8;          // waves per work group: one KV head each
+constexpr int NT = 64 * NW;
+constexpr int NTC = 256;       // combine kernel block
+constexpr int SUB = 32;        // keys per wave step
+constexpr int DVS = 80;        // LDS row stride of a wave's K / V block (160 B)
+
+// max / sum over lanes l, l^16, l^32, l^48 (the 4 lanes of one MFMA column)
+__device__ __forceinline__ float col_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 16-byte non-temporal load (global_load_dwordx4 ... nt): streamed once, kept out of the caches
+__device__ __forceinline__ uint4 ldg16_nt(const bf16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <bool ROTQ>
 __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds_v[4][SUB * DVS];
-  __shared__ float red_m[4][8];
-  __shared__ float red_l[4][8];
-  __shared__ float red_o[4][8][kHeadDim];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_v[NW][SUB * DVS];
 
-  const int g = blockIdx.x;       // KV heads fastest: the 8 groups reading the same cache rows run together
-  const int split = blockIdx.y;
-  const int n = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int n = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = blockIdx.z * NW + wave;
   const int col = lane & 15, grp = lane >> 4;
+  if (g >= p.num_kv_heads) return;
 
   const int L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
   const int lo = (p.window > 0) ? max(0, L - p.window) : 0;
@@ -43,11 +67,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   if (split >= nsplit) return;
   const int c0 = lo + split * p.chunk;
   const int c1 = min(c0 + p.chunk, L);
-  const int per_wave = p.chunk / 4;
-  const int w0 = c0 + wave * per_wave;
   const float sl = p.scale_log2;
 
-  // q fragment (B operand): column col = query head 8g + col for col < 8
   bf16x8_t qf[2];
   {
     uint4 y1 = make_uint4(0, 0, 0, 0), y2 = make_uint4(0, 0, 0, 0);
@@ -74,43 +95,47 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // K (A operand: rows = keys, k = d) and V rows for the 32 keys at s0; rows
-  // at or beyond c1 read as zero
-  bf16x8_t ka[2][2];
-  uint4 vr[4];
+  uint4 kr[4], vr[4];
   auto load_block = [&](int s0) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = s0 + kb * 16 + col;
-      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-      if (key < c1) {
-        const bf16_t* kp = kbase + (int64_t)key * p.kv_sp + 8 * grp;
-        a0 = ldg16(kp);
-        a1 = ldg16(kp + 32);
-      }
-      ka[kb][0] = as_bf16x8(a0);
-      ka[kb][1] = as_bf16x8(a1);
-    }
-    // V rows s0 .. s0+31: lane -> rows (lane>>3) + 8i, 16 B chunk lane&7
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = s0 + (lane >> 3) + 8 * i;
+      kr[i] = make_uint4(0, 0, 0, 0);
       vr[i] = make_uint4(0, 0, 0, 0);
-      if (key < c1) vr[i] = ldg16(vbase + (int64_t)key * p.kv_sp + 8 * (lane & 7));
+      if (key < c1) {
+        kr[i] = ldg16_nt(kbase + (int64_t)key * p.kv_sp + 8 * (lane & 7));
+        vr[i] = ldg16_nt(vbase + (int64_t)key * p.kv_sp + 8 * (lane & 7));
+      }
     }
   };
-  const int w1 = min(w0 + per_wave, c1);   // this wave's keys: [w0, w1)
-  if (w0 < w1) load_block(w0);
-  for (int s0 = w0; s0 < w1; s0 += SUB) {
-    const bf16x8_t k00 = ka[0][0], k01 = ka[0][1], k10 = ka[1][0], k11 = ka[1][1];
-    const uint4 v0 = vr[0], v1 = vr[1], v2 = vr[2], v3 = vr[3];
-    if (s0 + SUB < w1) load_block(s0 + SUB);   // next block in flight during this one
+  if (c0 < c1) load_block(c0);
+  for (int s0 = c0; s0 < c1; s0 += SUB) {
+    // K rows -> LDS -> MFMA A fragments
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 8 * i) * DVS + 8 * (lane & 7)) = kr[i];
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    bf16x8_t ka[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      ka[kb][0] = *reinterpret_cast<const bf16x8_t*>(vl + (kb * 16 + col) * DVS + 8 * grp);
+      ka[kb][1] = *reinterpret_cast<const bf16x8_t*>(vl + (kb * 16 + col) * DVS + 32 + 8 * grp);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // V rows -> the same LDS block (the K fragments are in registers now), read back transposed
+    // below; the staging registers are then free for the next step's loads
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 8 * i) * DVS + 8 * (lane & 7)) = vr[i];
+    if (s0 + SUB < c1) load_block(s0 + SUB);
     f32x4_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-      z = mfma16(kb ? k10 : k00, qf[0], z);
-      sacc[kb] = mfma16(kb ? k11 : k01, qf[1], z);
+      z = mfma16(ka[kb][0], qf[0], z);
+      sacc[kb] = mfma16(ka[kb][1], qf[1], z);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -121,21 +146,18 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
         sacc[kb][r] = (key < c1) ? sacc[kb][r] : -INFINITY;
         mx = fmaxf(mx, sacc[kb][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = col_max(mx);
     const float mnew = fmaxf(m, mx * sl);
     const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float f = __builtin_amdgcn_exp2f(m - mu);   // m = -inf -> 0
+    const float f = __builtin_amdgcn_exp2f(m - mu);
     uint32_t w[4];
     float psum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][0], sl, -mu));
-      float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][1], sl, -mu));
-      float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2], sl, -mu));
-      float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][3], sl, -mu));
-      w[2 * kb] = pack_bf16x2(e0, e1);
-      w[2 * kb + 1] = pack_bf16x2(e2, e3);
+      w[2 * kb] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][0], sl, -mu)),
+                              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][1], sl, -mu)));
+      w[2 * kb + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2], sl, -mu)),
+                                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][3], sl, -mu)));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) psum = add_bf16x2(w[i], psum);
@@ -144,12 +166,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] *= f;
     const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-
-    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 0) * DVS + 8 * (lane & 7)) = v0;
-    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 8) * DVS + 8 * (lane & 7)) = v1;
-    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 16) * DVS + 8 * (lane & 7)) = v2;
-    *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 24) * DVS + 8 * (lane & 7)) = v3;
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -160,48 +177,23 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
       oacc[db] = mfma16(a, pf, oacc[db]);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();   // reads done before the next step overwrites the block
+    __builtin_amdgcn_wave_barrier();
   }
-
-  // ---- merge the 4 waves ----
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = col_sum(lsum);
   if (col < kGroup) {
-    if (grp == 0) {
-      red_m[wave][col] = m;
-      red_l[wave][col] = lsum;
-    }
+    const int64_t slot = (((int64_t)n * p.num_kv_heads + g) * p.num_splits + split) * kGroup + col;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[wave][col][16 * db + 4 * grp + r] = oacc[db][r];
+      *reinterpret_cast<f32x4_t*>(p.part_o + slot * kHeadDim + 16 * db + 4 * grp) = oacc[db];
+    if (grp == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m, lsum);
   }
-  __syncthreads();
-  // thread -> (head c, two dims)
-  const int c = tid >> 5;
-  const int d0 = 2 * (tid & 31);
-  float M = -INFINITY;
-#pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, red_m[w2][c]);
-  const float Mu = (M == -INFINITY) ? 0.0f : M;
-  float lt = 0.0f, o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) {
-    const float f = __builtin_amdgcn_exp2f(red_m[w2][c] - Mu);
-    lt += red_l[w2][c] * f;
-    o0 += red_o[w2][c][d0] * f;
-    o1 += red_o[w2][c][d0 + 1] * f;
-  }
-  const int64_t slot = (((int64_t)n * p.num_kv_heads + g) * p.num_splits + split) * kGroup + c;
-  *reinterpret_cast<float2*>(p.part_o + slot * kHeadDim + d0) = make_float2(o0, o1);
-  if ((tid & 31) == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(M, lt);
 }
 
 // One wave per (sequence, query head). Splits across lanes for the max and the
 // weights, then lane = head dim for the weighted sum of the partial outputs.
-__global__ __launch_bounds__(NT) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(NTC) void decode_combine_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
-  const int idx = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  const int idx = blockIdx.x * (NTC / 64) + (threadIdx.x >> 6);
   const int Hq = p.num_kv_heads * kGroup;
   if (idx >= p.num_seqs * Hq) return;
   const int n = idx / Hq;
@@ -255,7 +247,7 @@ __global__ __launch_bounds__(NT) void decode_combine_kernel(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
-  dim3 grid(p.num_kv_heads, p.num_splits, p.num_seqs);
+  dim3 grid(p.num_splits, p.num_seqs, (p.num_kv_heads + NW - 1) / NW);
   if (p.table)
     hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(NT), 0, stream, p);
   else
@@ -263,7 +255,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = p.num_seqs * p.num_kv_heads * kGroup;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((waves + 3) / 4), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((waves + 3) / 4), dim3(NTC), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -161,9 +161,9 @@ def test_decode_argument_errors(lib):
 
 
 def test_decode_workspace_size(lib):
-    # 64 sequences x 64 heads x ceil(32768 / 1024) splits x (64 + 2) floats
+    # 64 sequences x 64 heads x ceil(32768 / 512) splits x (64 + 2) floats
     ws = lib.gptoss_attn_decode_workspace_size(64, 64, 32768, 0)
-    assert ws == 64 * 64 * 32 * 64 * 4 + 64 * 64 * 32 * 2 * 4
+    assert ws == 64 * 64 * 64 * 64 * 4 + 64 * 64 * 64 * 2 * 4
     assert lib.gptoss_attn_decode_workspace_size(2, 64, 1000, 3) >= 2 * 64 * 3 * 66 * 4
     assert lib.gptoss_attn_decode_workspace_size(2, 64, 0, 0) == 0
 
