@@ -35,8 +35,10 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 WINDOW = 128
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["attention_yarn_rope_amd/csrc/prefill.hip", "attention_yarn_rope_amd/csrc/common.h",
-                  "attention_yarn_rope_amd/csrc/decode.hip"]
+KERNEL_SOURCES = {   # the sources a kernel's counters depend on
+    "prefill": ["attention_yarn_rope_amd/csrc/prefill.hip", "attention_yarn_rope_amd/csrc/common.h"],
+    "decode": ["attention_yarn_rope_amd/csrc/decode.hip", "attention_yarn_rope_amd/csrc/common.h"],
+}
 
 
 def log(msg):
@@ -51,7 +53,7 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def counters_traffic(name, launches_bytes_unit=1):
+def counters_traffic(name, kernel):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
 
     profiles/<name>.counters.json holds FETCH_SIZE and WRITE_SIZE (KiB per
@@ -64,7 +66,7 @@ def counters_traffic(name, launches_bytes_unit=1):
         return None
     with open(path) as f:
         c = json.load(f)
-    if c.get("source_hash") != source_hash(KERNEL_SOURCES):
+    if c.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return c["traffic_bytes_per_launch"]
 
@@ -262,7 +264,7 @@ def main():
             "ms_full_layer": round(ms_df, 4), "ms_window_layer": round(ms_dw, 4),
             "bytes_full_layer": b_full, "bytes_window_layer": b_win,
             "window_layer_GBps": round(b_win / (ms_dw * 1e-3) / 1e9, 1),
-            "traffic": counters_traffic("decode_split_full_64seq"),
+            "traffic": counters_traffic("decode_full_64seq", "decode"),
         }
         log(f"[bench] decode full {ms_df:.3f} ms = {gbs:.0f} GB/s; window {ms_dw:.4f} ms")
         del kc, vc
@@ -295,7 +297,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": counters_traffic("prefill_full_dense_B4_S4096"),
+            "traffic": counters_traffic("prefill_full_dense_B4_S4096", "prefill"),
             "flops_per_launch": flops_full,
             "ms_per_launch": round(ms_full, 4),
         },
