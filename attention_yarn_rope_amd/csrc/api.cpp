@@ -237,6 +237,7 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
   const bool thd = desc->layout == GPTOSS_THD;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  const int bq = kPrefillBQ;
 
   PrefillParams p;
   memset(&p, 0, sizeof p);
@@ -264,14 +265,14 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
     ws += round_up((size_t)max_items * sizeof(int2));
     int32_t* count = reinterpret_cast<int32_t*>(ws);
     ws += kAlign;
-    st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, max_items, work, count, s),
+    st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, bq, max_items, work, count, s),
                     "THD schedule kernel");
     if (st != GPTOSS_OK) return st;
     p.work = work;
     p.work_count = count;
     p.q_blocks = max_items;
   } else {
-    p.q_blocks = (desc->seqlen + kPrefillBQ - 1) / kPrefillBQ;
+    p.q_blocks = (desc->seqlen + bq - 1) / bq;
   }
 
   if (table && krot != KROT_FUSED) {
@@ -307,10 +308,10 @@ gptoss_status gptoss_attn_prefill(const gptoss_seq_desc* desc, const void* q, co
                                   int32_t window, const void* table, int32_t table_rows, int32_t rotary_dim,
                                   void* out, const int64_t o_strides[3], void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  // K rotation: fused into the tile loads for window layers (few tiles per
-  // query block); one separate pass for full-causal layers, where every key
-  // tile is visited by many query blocks.
-  const int krot = window > 0 ? KROT_FUSED : KROT_NONE;
+  // K rotation: one separate pass into the workspace for both layer types.
+  // Rotating inside the tile loads was measured slower on gfx950 even for
+  // window layers, where each key tile is staged only about three times.
+  const int krot = KROT_NONE;
   return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, sinks, softmax_scale, window, table,
                       table_rows, rotary_dim, out, o_strides, workspace, workspace_bytes, krot, stream);
 }
@@ -324,7 +325,7 @@ gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc, const void* q,
                                      void* stream) {
   int krot;
   switch (k_rotation) {
-    case GPTOSS_KROT_AUTO: krot = window > 0 ? KROT_FUSED : KROT_NONE; break;
+    case GPTOSS_KROT_AUTO: krot = KROT_NONE; break;
     case GPTOSS_KROT_FUSED: krot = KROT_FUSED; break;
     case GPTOSS_KROT_SEPARATE: krot = KROT_NONE; break;
     default: return fail(GPTOSS_ERR_SHAPE, "k_rotation %d is not a gptoss_k_rotation value", k_rotation);

@@ -46,15 +46,17 @@ __device__ __forceinline__ float two_sum_err(float a, float b, float s) {
 }
 #pragma clang fp contract(on)
 
-// Exact-rounding fix-up of s = RN_fp32(a + b) where a and b are exact fp32 values.
+// Exact-rounding fix-up of s = RN_fp32(a + b) where a and b are exact fp32
+// values (branch free: a select, not a branch, per element).
 __device__ __forceinline__ float fix_bf16_tie(float a, float b, float s) {
-  uint32_t u = __float_as_uint(s);
-  if ((u & 0xFFFFu) == 0x8000u) {
-    float e = two_sum_err(a, b, s);
-    if (e != 0.0f) u += ((e > 0.0f) == (s > 0.0f)) ? 1u : 0xFFFFFFFFu;
-  }
-  return __uint_as_float(u);
+  const uint32_t u = __float_as_uint(s);
+  const float e = two_sum_err(a, b, s);
+  const uint32_t step = (e == 0.0f) ? 0u : (((e > 0.0f) == (s > 0.0f)) ? 1u : 0xFFFFFFFFu);
+  return __uint_as_float(((u & 0xFFFFu) == 0x8000u) ? u + step : u);
 }
+
+// 0 exactly when the fp32 value's low 16 bits are 0x8000 (a bf16 midpoint)
+__device__ __forceinline__ uint32_t midpoint_key(float v) { return (__float_as_uint(v) << 16) ^ 0x80000000u; }
 
 // Rotate 8 pairs: x1 holds dims i..i+7, x2 dims i+32..i+39 (rotary_dim 64),
 // c / s the table's cos / sin for the same i. Writes rounded bf16 outputs.
@@ -67,7 +69,7 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
   uint32_t* py1 = reinterpret_cast<uint32_t*>(&y1);
   uint32_t* py2 = reinterpret_cast<uint32_t*>(&y2);
   float r1[8], r2[8];
-  bool tie = false;
+  uint32_t key = 0xFFFFFFFFu;   // min over the outputs of midpoint_key: 0 iff any sits on a midpoint
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
 #pragma unroll
@@ -82,10 +84,10 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
       float o2 = __builtin_fmaf(a2, cc, t2);   // RN(x2*C + x1*S)
       r1[2 * w + h] = o1;
       r2[2 * w + h] = o2;
-      tie = tie || ((__float_as_uint(o1) & 0xFFFFu) == 0x8000u) || ((__float_as_uint(o2) & 0xFFFFu) == 0x8000u);
+      key = min(key, min(midpoint_key(o1), midpoint_key(o2)));
     }
   }
-  if (tie) {  // rare: redo the affected elements with the exact fix-up
+  if (key == 0u) {  // rare: redo every element with the exact fix-up (a no-op off midpoints)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
 #pragma unroll

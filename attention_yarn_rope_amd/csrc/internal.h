@@ -54,7 +54,8 @@ struct PrefillParams {
 };
 enum KRotation { KROT_NONE = 0, KROT_FUSED = 1 };
 hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_t stream);
-hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_items,
+// THD work list of (sequence, block of bq query positions), longest first
+hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t bq, int32_t max_items,
                                int2* work, int32_t* work_count, hipStream_t stream);
 constexpr int kPrefillBQ = 32;   // query positions per work item
 

@@ -99,62 +99,27 @@ void prefill_kernel(PrefillParams p) {
   const int ntiles = (kv_hi - kv_lo + NK - 1) / NK;
   const float sl = p.scale_log2;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), rotated on load ----
-  bf16x8_t qf[4][2];
-  int qpos[2];
-  qpos[0] = q0 + col;
-  qpos[1] = q0 + 16 + col;
-  float ref[4], lsum[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int head = g * kGroup + wave * 2 + (cb >> 1);
-    const int pos = qpos[cb & 1];
-    uint4 y1 = make_uint4(0, 0, 0, 0), y2 = make_uint4(0, 0, 0, 0);
-    if (pos <= qlast) {
-      const bf16_t* qp = p.q + bb_off_q + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh;
-      uint4 x1 = ldg16(qp + 8 * grp), x2 = ldg16(qp + 32 + 8 * grp);
-      if (ROTQ) {
-        const bf16_t* tp = p.table + (int64_t)min(pos, p.table_rows - 1) * kHeadDim + 8 * grp;
-        rope8(x1, x2, ldg16(tp), ldg16(tp + 32), y1, y2);
-      } else {
-        y1 = x1; y2 = x2;
-      }
-    }
-    qf[cb][0] = as_bf16x8(y1);
-    qf[cb][1] = as_bf16x8(y2);
-    // reference = the sink logit (log2 units); the sink term exp2(sigma - ref) = 1
-    // is counted once, in lane group 0. A sink of -inf contributes 0 (reference 0).
-    const float sink = __ldg(p.sinks + head) * kLog2e;
-    const bool has_sink = sink > -INFINITY;
-    ref[cb] = has_sink ? sink : 0.0f;
-    lsum[cb] = (grp == 0 && has_sink) ? 1.0f : 0.0f;
-  }
-
-  f32x4_t oacc[4][4];  // [d block][column block]
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) oacc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // ---- K/V tile staging: thread -> (row, 8-dim chunk cc and cc + 4) ----
+  // ---- K/V tile staging: thread -> (row, 8-dim chunk cc and cc + 4). Rows
+  // past the item's last key re-read that key: they lie after every query of
+  // the item, so the causal mask gives them weight exactly 0. ----
   const int srow = tid >> 2;
   const int scc = tid & 3;
+  const bf16_t* k_first = p.k + bb_off_k + (int64_t)(ts + kv_lo + srow) * p.k_st + (int64_t)g * p.k_sh + 8 * scc;
+  const bf16_t* v_first = p.v + bb_off_v + (int64_t)(ts + kv_lo + srow) * p.v_st + (int64_t)g * p.v_sh + 8 * scc;
+  const bf16_t* k_last = p.k + bb_off_k + (int64_t)(ts + kv_hi - 1) * p.k_st + (int64_t)g * p.k_sh + 8 * scc;
+  const bf16_t* v_last = p.v + bb_off_v + (int64_t)(ts + kv_hi - 1) * p.v_st + (int64_t)g * p.v_sh + 8 * scc;
+  const int64_t k_step = (int64_t)NK * p.k_st, v_step = (int64_t)NK * p.v_st;
   uint4 sk1, sk2, sv1, sv2, sc, ss;
   auto load_tile = [&](int t) {
     const int kpos = kv_lo + t * NK + srow;
-    if (kpos < kv_hi) {
-      const int64_t tok = ts + kpos;
-      const bf16_t* kp = p.k + bb_off_k + tok * p.k_st + (int64_t)g * p.k_sh + 8 * scc;
-      const bf16_t* vp = p.v + bb_off_v + tok * p.v_st + (int64_t)g * p.v_sh + 8 * scc;
-      sk1 = ldg16(kp); sk2 = ldg16(kp + 32);
-      sv1 = ldg16(vp); sv2 = ldg16(vp + 32);
-      if (ROTK) {
-        const bf16_t* tp = p.table + (int64_t)min(kpos, p.table_rows - 1) * kHeadDim + 8 * scc;
-        sc = ldg16(tp); ss = ldg16(tp + 32);
-      }
-    } else {
-      sk1 = sk2 = sv1 = sv2 = make_uint4(0, 0, 0, 0);
-      sc = ss = make_uint4(0, 0, 0, 0);
+    const bool in = kpos < kv_hi;
+    const bf16_t* kp = in ? k_first + t * k_step : k_last;
+    const bf16_t* vp = in ? v_first + t * v_step : v_last;
+    sk1 = ldg16(kp); sk2 = ldg16(kp + 32);
+    sv1 = ldg16(vp); sv2 = ldg16(vp + 32);
+    if (ROTK) {
+      const bf16_t* tp = p.table + (int64_t)min(min(kpos, kv_hi - 1), p.table_rows - 1) * kHeadDim + 8 * scc;
+      sc = ldg16(tp); ss = ldg16(tp + 32);
     }
   };
   auto store_tile = [&](int buf) {
@@ -168,10 +133,53 @@ void prefill_kernel(PrefillParams p) {
     *reinterpret_cast<uint4*>(vd + 32) = sv2;
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  // ---- Q fragments (B operand of S^T = K Q^T), rotated on load. Every
+  // independent load (the first K/V tile, q, table rows, sinks) is issued before
+  // any of them is used, so the work item pays one memory latency, not several.
+  // Rows past the end load a valid row and are never stored. ----
+  if (ntiles > 0) load_tile(0);
+  bf16x8_t qf[4][2];
+  int qpos[2];
+  qpos[0] = q0 + col;
+  qpos[1] = q0 + 16 + col;
+  uint4 qx[4][2], qt[4][2];
+  float sink_raw[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int head = g * kGroup + wave * 2 + (cb >> 1);
+    const int pos = min(qpos[cb & 1], qlast);
+    const bf16_t* qp = p.q + bb_off_q + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh;
+    qx[cb][0] = ldg16(qp + 8 * grp);
+    qx[cb][1] = ldg16(qp + 32 + 8 * grp);
+    if (ROTQ) {
+      const bf16_t* tp = p.table + (int64_t)min(pos, p.table_rows - 1) * kHeadDim + 8 * grp;
+      qt[cb][0] = ldg16(tp);
+      qt[cb][1] = ldg16(tp + 32);
+    }
+    sink_raw[cb] = __ldg(p.sinks + head);
   }
+  float ref[4], lsum[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    uint4 y1 = qx[cb][0], y2 = qx[cb][1];
+    if (ROTQ) rope8(qx[cb][0], qx[cb][1], qt[cb][0], qt[cb][1], y1, y2);
+    qf[cb][0] = as_bf16x8(y1);
+    qf[cb][1] = as_bf16x8(y2);
+    // reference = the sink logit (log2 units); the sink term exp2(sigma - ref) = 1
+    // is counted once, in lane group 0. A sink of -inf contributes 0 (reference 0).
+    const float sink = sink_raw[cb] * kLog2e;
+    const bool has_sink = sink > -INFINITY;
+    ref[cb] = has_sink ? sink : 0.0f;
+    lsum[cb] = (grp == 0 && has_sink) ? 1.0f : 0.0f;
+  }
+
+  f32x4_t oacc[4][4];  // [d block][column block]
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) oacc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) store_tile(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -309,13 +317,13 @@ void prefill_kernel(PrefillParams p) {
 }
 
 // Work list for packed sequences: every (sequence n, query block jb) with
-// jb < ceil(L_n / BQ), ordered by jb descending (the blocks with the most keys
+// jb < ceil(L_n / bq), ordered by jb descending (the blocks with the most keys
 // first), sequences ascending within one jb. One work group of 1024 threads.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedMaxBlocks = 8192;   // query blocks per sequence (L <= 262144)
 constexpr int kSchedMaxSeqs = 4096;
 
-__global__ __launch_bounds__(kSchedThreads) void thd_schedule_kernel(const int32_t* cu, int32_t num_seqs,
+__global__ __launch_bounds__(kSchedThreads) void thd_schedule_kernel(const int32_t* cu, int32_t num_seqs, int32_t bq,
                                                                      int32_t max_items, int2* work,
                                                                      int32_t* work_count) {
   __shared__ int32_t nb[kSchedMaxSeqs];
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(kSchedThreads) void thd_schedule_kernel(const int32
   for (int n = tid; n < num_seqs; n += kSchedThreads) {
     const int a = __ldg(cu + n), b = __ldg(cu + n + 1);
     const int len = max(b - a, 0);
-    const int q = min((len + BQ - 1) / BQ, kSchedMaxBlocks);
+    const int q = min((len + bq - 1) / bq, kSchedMaxBlocks);
     nb[n] = q;
     local_max = max(local_max, q);
   }
@@ -383,9 +391,9 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_items,
+hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t bq, int32_t max_items,
                                int2* work, int32_t* work_count, hipStream_t stream) {
-  hipLaunchKernelGGL(thd_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens, num_seqs,
+  hipLaunchKernelGGL(thd_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens, num_seqs, bq,
                      max_items, work, work_count);
   return hipGetLastError();
 }

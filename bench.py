@@ -286,7 +286,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "dense BSHD prefill B=4 S=4096 Hq=64 Hkv=8 D=64: YaRN table + full-causal layer + "
-                        "window-128 layer, q/k rotated inside attention",
+                        "window-128 layer, q and k rotated inside each attention call",
             "global_batch": q.shape[0], "seq_len": S, "parallelism": "none (1 GPU)",
             "k_rotation": args.k_rotation,
         },

@@ -180,8 +180,8 @@ gptoss_status gptoss_attn_prefill(const gptoss_seq_desc* desc,
 /*
  * gptoss_attn_prefill with an explicit choice of where k is rotated when a
  * table is given (results are bit-identical either way):
- *   GPTOSS_KROT_AUTO      the library's choice (fused for window layers,
- *                         separate for full-causal layers)
+ *   GPTOSS_KROT_AUTO      the library's choice (currently separate for both
+ *                         layer types: measured faster on gfx950)
  *   GPTOSS_KROT_FUSED     k rotated while each tile is staged into LDS
  *   GPTOSS_KROT_SEPARATE  k rotated once into the workspace, then attended
  * Any other value returns GPTOSS_ERR_SHAPE.
