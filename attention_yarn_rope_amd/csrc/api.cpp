@@ -334,25 +334,36 @@ gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc, const void* q,
                       table_rows, rotary_dim, out, o_strides, workspace, workspace_bytes, krot, stream);
 }
 
-// Keys per split (per KV head): a multiple of 128. Automatic: up to 512 keys,
-// which gives thousands of work groups for long caches while the partials stay
-// under 2% of the cache traffic.
-static int32_t decode_chunk(int32_t eff_len, int32_t num_splits) {
-  int32_t c = num_splits > 0 ? (eff_len + num_splits - 1) / num_splits : (eff_len < 512 ? eff_len : 512);
+// Keys per split when the caller fixes the number of splits: a multiple of 128.
+static int32_t decode_fixed_chunk(int32_t eff_len, int32_t num_splits) {
+  int32_t c = (eff_len + num_splits - 1) / num_splits;
   c = (c + 127) / 128 * 128;
   return c < 128 ? 128 : c;
 }
 
-// Upper bound of the splits any call with these sizes uses (window layers use fewer).
+// Upper bound of the splits any call with these sizes uses: the planned split
+// length is at least kDecodeMinChunk keys.
 static int64_t decode_split_cap(int32_t max_cache_len, int32_t num_splits) {
-  return num_splits > 0 ? num_splits : (max_cache_len + 511) / 512;
+  return num_splits > 0 ? num_splits : (max_cache_len + kDecodeMinChunk - 1) / kDecodeMinChunk;
+}
+
+// Work-group slots of the decode split kernel on the current device (2 per CU).
+static int32_t decode_slots() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return 2 * cus;
 }
 
 size_t gptoss_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_cache_len,
                                          int32_t num_splits) {
   if (num_seqs < 0 || num_q_heads < 0 || max_cache_len < 1 || num_splits < 0) return 0;
-  const size_t slots = (size_t)num_seqs * num_q_heads * decode_split_cap(max_cache_len, num_splits);
-  return round_up(slots * kHeadDim * sizeof(float)) + round_up(slots * 2 * sizeof(float));
+  const int64_t cap = decode_split_cap(max_cache_len, num_splits);
+  const size_t slots = (size_t)num_seqs * num_q_heads * cap;
+  // partials, then the split plan: 2 ints + one int2 per (sequence, split) item
+  return round_up(slots * kHeadDim * sizeof(float)) + round_up(slots * 2 * sizeof(float)) +
+         round_up(2 * sizeof(int32_t) + (size_t)num_seqs * cap * 2 * sizeof(int32_t));
 }
 
 gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -380,6 +391,9 @@ gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (o_strides[0] < 0 || o_strides[1] < 0 || (o_strides[0] & 1) || (o_strides[1] & 1) ||
       (reinterpret_cast<uintptr_t>(out) & 3))
     return fail(GPTOSS_ERR_UNSUPPORTED, "out must be 4-byte aligned with even strides");
+  if (kv_strides[1] < kHeadDim || (int64_t)max_cache_len * kv_strides[1] * 2 > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED,
+                "kv_strides[1] must be >= 64 and one sequence's rows must span less than 2 GiB");
   gptoss_status st = check_table(table, table_rows, rotary_dim, max_cache_len);
   if (st != GPTOSS_OK) return st;
   const size_t need = gptoss_attn_decode_workspace_size(num_seqs, num_q_heads, max_cache_len, num_splits);
@@ -402,14 +416,31 @@ gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t 
   p.sinks = sinks;
   p.table = static_cast<const uint16_t*>(table);
   p.table_rows = table_rows;
-  // window layers only ever read the last `window` rows: smaller chunks, fewer splits
+  // window layers only ever read the last `window` rows: fewer splits
   const int32_t eff = (window > 0 && window < max_cache_len) ? window : max_cache_len;
-  p.chunk = decode_chunk(eff, num_splits);
-  p.num_splits = (eff + p.chunk - 1) / p.chunk;   // <= decode_split_cap(): fits the workspace
+  if (num_splits == 1 || (num_splits == 0 && eff <= kDecodeMinChunk)) {
+    // one split per sequence (e.g. window layers): no plan, work item = sequence
+    p.direct_chunk = (eff + 127) / 128 * 128;
+    p.num_splits = 1;
+  } else if (num_splits > 0) {
+    p.chunk_fixed = decode_fixed_chunk(eff, num_splits);
+    p.num_splits = (eff + p.chunk_fixed - 1) / p.chunk_fixed;
+  } else {
+    // planned on the device from the cache lengths: about 1.3 work items per slot
+    p.chunk_fixed = 0;
+    p.target_chunks = decode_slots() * 13 / 10;
+    p.num_splits = (eff + kDecodeMinChunk - 1) / kDecodeMinChunk;
+  }
+  // p.num_splits <= decode_split_cap(): the partial buffers fit the workspace
   char* ws = static_cast<char*>(workspace);
-  const size_t slots = (size_t)num_seqs * num_q_heads * p.num_splits;
+  const size_t cap = (size_t)num_seqs * num_q_heads * decode_split_cap(max_cache_len, num_splits);
   p.part_o = reinterpret_cast<float*>(ws);
-  p.part_ml = reinterpret_cast<float*>(ws + round_up(slots * kHeadDim * sizeof(float)));
+  p.part_ml = reinterpret_cast<float*>(ws + round_up(cap * kHeadDim * sizeof(float)));
+  p.plan = reinterpret_cast<int32_t*>(ws + round_up(cap * kHeadDim * sizeof(float)) + round_up(cap * 2 * sizeof(float)));
+  // work groups: enough for every item of the largest plan, at most two per slot (they loop)
+  const int64_t max_items = (int64_t)num_seqs * p.num_splits;
+  const int64_t groups = (int64_t)decode_slots() * 2;
+  p.max_items = (int32_t)(max_items < groups ? max_items : groups);
   p.o = static_cast<uint16_t*>(out);
   p.o_sn = o_strides[0]; p.o_sh = o_strides[1];
   return hip_status(launch_decode(p, static_cast<hipStream_t>(stream)), "decode kernels");

@@ -5,14 +5,15 @@
 // Transformers v4.55.0 release notes, "Architecture").
 //
 // Split kernel: one work group per (key chunk, sequence, group of 8 KV heads);
+// the chunk length comes from the plan kernel below;
 // wave w takes KV head w, so the group streams whole 1 KB cache rows (8 heads
 // x 128 B) and each K/V row of a head is read from HBM exactly once for the 8
-// query heads that share it. Rows are fetched in full 128 B lines with
-// non-temporal loads (read-once data), 32 keys per step, the next step's loads
-// in flight while the current one computes. K and V pass through one per-wave
-// LDS block: K is read back as MFMA A fragments for S^T = K Q^T
-// (v_mfma_f32_16x16x32_bf16, 8 heads padded to 16 columns), V transposed with
-// ds_read_b64_tr_b16 for O^T = V^T P^T. Exact online softmax per step; each
+// query heads that share it. Rows are fetched with non-temporal loads
+// (read-once data) in whole 128-byte rows, 32 keys per step, the next step's
+// loads in flight while the current one computes. K and V pass
+// through one per-wave LDS block: K is read back as MFMA A fragments for
+// S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 8 heads padded to 16 columns), V
+// transposed with ds_read_b64_tr_b16 for O^T = V^T P^T. Exact online softmax per step; each
 // wave writes one unnormalised partial (m, l, acc[64]) per query head.
 // Combine kernel: per (sequence, query head) it merges the partials and adds
 // the sink exactly once: M = max(sigma, m_s), l = exp(sigma - M) + sum l_s
@@ -43,10 +44,15 @@ __device__ __forceinline__ float col_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// 16-byte non-temporal load (global_load_dwordx4 ... nt): streamed once, kept out of the caches
-__device__ __forceinline__ uint4 ldg16_nt(const bf16_t* p) {
+// Buffer resource over `bytes` bytes from `base` (raw, stride 0; the gfx9 word 3).
+// A buffer load whose offset lies past `bytes` returns zeros instead of reading.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// 16-byte non-temporal buffer load (buffer_load_dwordx4 ... nt): read-once data
+__device__ __forceinline__ uint4 ldb16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -54,62 +60,72 @@ template <bool ROTQ>
 __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[NW][SUB * DVS];
 
-  const int split = blockIdx.x;
-  const int n = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.z * NW + wave;
   const int col = lane & 15, grp = lane >> 4;
   if (g >= p.num_kv_heads) return;
-
+  const bool direct = p.direct_chunk > 0;
+  const int chunk = direct ? p.direct_chunk : __builtin_amdgcn_readfirstlane(p.plan[0]);
+  const int items = direct ? p.num_seqs : __builtin_amdgcn_readfirstlane(p.plan[1]);
+  const int2* work = reinterpret_cast<const int2*>(p.plan + 2);
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  const int2 w = direct ? make_int2(it, 0) : work[it];
+  const int n = __builtin_amdgcn_readfirstlane(w.x);
+  const int split = __builtin_amdgcn_readfirstlane(w.y);
   const int L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
   const int lo = (p.window > 0) ? max(0, L - p.window) : 0;
-  const int nsplit = (L - lo + p.chunk - 1) / p.chunk;
-  if (split >= nsplit) return;
-  const int c0 = lo + split * p.chunk;
-  const int c1 = min(c0 + p.chunk, L);
+  const int c0 = lo + split * chunk;
+  const int c1 = min(c0 + chunk, L);
   const float sl = p.scale_log2;
 
+  const char* kbase = reinterpret_cast<const char*>(p.k + (int64_t)n * p.kv_sn + (int64_t)g * p.kv_sh);
+  const char* vbase = reinterpret_cast<const char*>(p.v + (int64_t)n * p.kv_sn + (int64_t)g * p.kv_sh);
+  bf16_t* vl = lds_v[wave];
+  const int32_t row_bytes = (int32_t)p.kv_sp * 2;   // < 2^31 over a whole sequence (host check)
+  // per-lane byte offset inside a step: row (lane >> 3) + 8 i, 16-byte chunk lane & 7,
+  // so one load instruction moves 8 whole 128-byte rows of this head
+  const uint32_t roff = (uint32_t)((lane >> 3) * row_bytes + 16 * (lane & 7));
+
+  // The rows of step s + 1 are requested as soon as step s has moved its rows
+  // into LDS. The buffer range ends after key c1 - 1, so rows past the chunk
+  // read as zeros.
+  uint4 kr[4], vr[4];
+  auto load_block = [&](int s0) __attribute__((always_inline)) {
+    const int64_t start = (int64_t)s0 * row_bytes;
+    const int32_t bytes = (c1 > s0) ? (c1 - s0 - 1) * row_bytes + 2 * kHeadDim : 0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + start, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + start, bytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = ldb16_nt(rk, roff + (uint32_t)(i * 8 * row_bytes));
+      vr[i] = ldb16_nt(rv, roff + (uint32_t)(i * 8 * row_bytes));
+    }
+  };
+  // the first step's rows are requested before q, so both latencies overlap
+  if (c0 < c1) load_block(c0);
+
+  // Q fragments (B operand, 8 query heads in columns 0..7; columns 8..15 are
+  // zero padding). Every lane loads a valid row so the loads need no branch.
   bf16x8_t qf[2];
   {
-    uint4 y1 = make_uint4(0, 0, 0, 0), y2 = make_uint4(0, 0, 0, 0);
-    if (col < kGroup) {
-      const bf16_t* qp = p.q + (int64_t)n * p.q_sn + (int64_t)(g * kGroup + col) * p.q_sh;
-      uint4 x1 = ldg16(qp + 8 * grp), x2 = ldg16(qp + 32 + 8 * grp);
-      if (ROTQ) {
-        const bf16_t* tp = p.table + (int64_t)min(max(L - 1, 0), p.table_rows - 1) * kHeadDim + 8 * grp;
-        rope8(x1, x2, ldg16(tp), ldg16(tp + 32), y1, y2);
-      } else {
-        y1 = x1; y2 = x2;
-      }
+    const bf16_t* qp = p.q + (int64_t)n * p.q_sn + (int64_t)(g * kGroup + (col & (kGroup - 1))) * p.q_sh;
+    const uint4 x1 = ldg16(qp + 8 * grp), x2 = ldg16(qp + 32 + 8 * grp);
+    uint4 y1 = x1, y2 = x2;
+    if (ROTQ) {
+      const bf16_t* tp = p.table + (int64_t)min(max(L - 1, 0), p.table_rows - 1) * kHeadDim + 8 * grp;
+      rope8(x1, x2, ldg16(tp), ldg16(tp + 32), y1, y2);
     }
-    qf[0] = as_bf16x8(y1);
-    qf[1] = as_bf16x8(y2);
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    qf[0] = as_bf16x8(col < kGroup ? y1 : zero);
+    qf[1] = as_bf16x8(col < kGroup ? y2 : zero);
   }
-
-  const bf16_t* kbase = p.k + (int64_t)n * p.kv_sn + (int64_t)g * p.kv_sh;
-  const bf16_t* vbase = p.v + (int64_t)n * p.kv_sn + (int64_t)g * p.kv_sh;
-  bf16_t* vl = lds_v[wave];
 
   float m = -INFINITY, lsum = 0.0f;
   f32x4_t oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 kr[4], vr[4];
-  auto load_block = [&](int s0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = s0 + (lane >> 3) + 8 * i;
-      kr[i] = make_uint4(0, 0, 0, 0);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (key < c1) {
-        kr[i] = ldg16_nt(kbase + (int64_t)key * p.kv_sp + 8 * (lane & 7));
-        vr[i] = ldg16_nt(vbase + (int64_t)key * p.kv_sp + 8 * (lane & 7));
-      }
-    }
-  };
-  if (c0 < c1) load_block(c0);
-  for (int s0 = c0; s0 < c1; s0 += SUB) {
+  auto step = [&](int s0) __attribute__((always_inline)) {
     // K rows -> LDS -> MFMA A fragments
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -124,8 +140,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
-    // V rows -> the same LDS block (the K fragments are in registers now), read back transposed
-    // below; the staging registers are then free for the next step's loads
+    // V rows -> the same LDS block (the K fragments are in registers now), read back
+    // transposed below; the staging registers are then free for the next step's rows
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(vl + ((lane >> 3) + 8 * i) * DVS + 8 * (lane & 7)) = vr[i];
@@ -178,7 +194,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
-  }
+  };
+  for (int s0 = c0; s0 < c1; s0 += SUB) step(s0);
   lsum = col_sum(lsum);
   if (col < kGroup) {
     const int64_t slot = (((int64_t)n * p.num_kv_heads + g) * p.num_splits + split) * kGroup + col;
@@ -187,6 +204,83 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
       *reinterpret_cast<f32x4_t*>(p.part_o + slot * kHeadDim + 16 * db + 4 * grp) = oacc[db];
     if (grp == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m, lsum);
   }
+  }   // work items
+}
+
+// Split planning. Every work group ends with stores of its partials, whose
+// completion it waits for; thousands of small splits pay that wait thousands
+// of times, a few hundred large ones leave the machine idle at the end. The
+// plan kernel reads the cache lengths and picks the split length so that the
+// call has about target_chunks (sequence, split) items: total visible keys /
+// target_chunks, rounded up to a multiple of 128, at least kDecodeMinChunk (so
+// the partial buffers sized on the host always suffice). A caller-given split
+// count is used as is. It then writes the list of items, the full-length
+// splits first and each sequence's shorter last split after them, so the split
+// kernel's work groups take real work only and the short items run last.
+// plan[0] = keys per split, plan[1] = item count, plan[2..] = int2 (sequence, split).
+constexpr int kPlanThreads = 256;
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams p) {
+  __shared__ long long part[kPlanThreads];
+  __shared__ int scan_full[kPlanThreads], scan_part[kPlanThreads];
+  __shared__ int chunk_s;
+  const int t = threadIdx.x;
+  auto eff_len = [&](int n) {
+    const int L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
+    return (p.window > 0) ? min(L, p.window) : L;
+  };
+  long long total = 0;
+  for (int n = t; n < p.num_seqs; n += kPlanThreads) total += eff_len(n);
+  part[t] = total;
+  __syncthreads();
+  for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
+    if (t < off) part[t] += part[t + off];
+    __syncthreads();
+  }
+  if (t == 0) {
+    int chunk = p.chunk_fixed;
+    if (chunk <= 0) {
+      const long long want = (part[0] + p.target_chunks - 1) / max(p.target_chunks, 1);
+      long long c = (want + 127) / 128 * 128;
+      c = c < kDecodeMinChunk ? kDecodeMinChunk : c;
+      const long long cap = ((long long)p.max_cache_len + 127) / 128 * 128;
+      chunk = (int)(c > cap ? (cap > kDecodeMinChunk ? cap : kDecodeMinChunk) : c);
+    }
+    chunk_s = chunk;
+    p.plan[0] = chunk;
+  }
+  __syncthreads();
+  const int chunk = chunk_s;
+  // thread t owns sequences [n0, n1)
+  const int per = (p.num_seqs + kPlanThreads - 1) / kPlanThreads;
+  const int n0 = min(t * per, p.num_seqs), n1 = min(n0 + per, p.num_seqs);
+  int nf = 0, np = 0;
+  for (int n = n0; n < n1; ++n) {
+    const int e = eff_len(n);
+    nf += e / chunk;
+    np += (e % chunk) != 0;
+  }
+  scan_full[t] = nf;
+  scan_part[t] = np;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {   // inclusive scans
+    const int a = (t >= off) ? scan_full[t - off] : 0;
+    const int b = (t >= off) ? scan_part[t - off] : 0;
+    __syncthreads();
+    scan_full[t] += a;
+    scan_part[t] += b;
+    __syncthreads();
+  }
+  const int total_full = scan_full[kPlanThreads - 1];
+  int pf = scan_full[t] - nf;                 // exclusive prefix: first slot of this thread
+  int pp = total_full + scan_part[t] - np;
+  int2* work = reinterpret_cast<int2*>(p.plan + 2);
+  for (int n = n0; n < n1; ++n) {
+    const int e = eff_len(n);
+    const int full = e / chunk;
+    for (int s = 0; s < full; ++s) work[pf++] = make_int2(n, s);
+    if (e % chunk) work[pp++] = make_int2(n, full);
+  }
+  if (t == kPlanThreads - 1) p.plan[1] = total_full + scan_part[kPlanThreads - 1];
 }
 
 // One wave per (sequence, query head). Splits across lanes for the max and the
@@ -201,7 +295,8 @@ __global__ __launch_bounds__(NTC) void decode_combine_kernel(DecodeParams p) {
   const int g = h / kGroup, c = h - g * kGroup;
   const int L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
   const int lo = (p.window > 0) ? max(0, L - p.window) : 0;
-  const int nsplit = min((L - lo + p.chunk - 1) / p.chunk, p.num_splits);
+  const int chunk = p.direct_chunk > 0 ? p.direct_chunk : *p.plan;
+  const int nsplit = min((L - lo + chunk - 1) / chunk, p.num_splits);
   const float sig = __ldg(p.sinks + h) * kLog2e;
   const int64_t base = ((int64_t)n * p.num_kv_heads + g) * p.num_splits;
   float M = sig;
@@ -247,12 +342,19 @@ __global__ __launch_bounds__(NTC) void decode_combine_kernel(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
-  dim3 grid(p.num_splits, p.num_seqs, (p.num_kv_heads + NW - 1) / NW);
+  hipError_t e;
+  if (p.direct_chunk <= 0) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // one work group per planned item (at most max_items of them), looping if there are more
+  dim3 grid((unsigned)p.max_items, 1, (p.num_kv_heads + NW - 1) / NW);
   if (p.table)
     hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(NT), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(NT), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = p.num_seqs * p.num_kv_heads * kGroup;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((waves + 3) / 4), dim3(NTC), 0, stream, p);

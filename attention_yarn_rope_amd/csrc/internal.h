@@ -71,11 +71,17 @@ struct DecodeParams {
   const float* sinks;
   const uint16_t* table;
   int32_t table_rows;
-  int32_t num_splits, chunk;     // keys per split (multiple of 128)
+  int32_t num_splits;            // split slots per (sequence, KV head) in the partial buffers
+  int32_t chunk_fixed;           // > 0: keys per split given by the caller; 0: planned on the device
+  int32_t target_chunks;         // planned: aim for about this many (sequence, split) work items
+  int32_t* plan;                 // device: keys per split, item count, then int2 (sequence, split) items
+  int32_t max_items;             // work groups launched for the split kernel
+  int32_t direct_chunk;          // > 0: one split of this many keys per sequence, no plan (item = sequence)
   float* part_o;                 // [N, Hkv, splits, 8, 64]
   float* part_ml;                // [N, Hkv, splits, 8, 2]
   uint16_t* o; int64_t o_sn, o_sh;
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+constexpr int kDecodeMinChunk = 512;   // smallest planned split (keys)
 
 }  // namespace gptoss

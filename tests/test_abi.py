@@ -161,9 +161,11 @@ def test_decode_argument_errors(lib):
 
 
 def test_decode_workspace_size(lib):
-    # 64 sequences x 64 heads x ceil(32768 / 512) splits x (64 + 2) floats
+    # 64 sequences x 64 heads x ceil(32768 / 512) splits x (64 + 2) floats, plus the
+    # split plan: 2 ints and one (sequence, split) int pair per item, rounded to 256 bytes
     ws = lib.gptoss_attn_decode_workspace_size(64, 64, 32768, 0)
-    assert ws == 64 * 64 * 64 * 64 * 4 + 64 * 64 * 64 * 2 * 4
+    plan = (2 * 4 + 64 * 64 * 8 + 255) // 256 * 256
+    assert ws == 64 * 64 * 64 * 64 * 4 + 64 * 64 * 64 * 2 * 4 + plan
     assert lib.gptoss_attn_decode_workspace_size(2, 64, 1000, 3) >= 2 * 64 * 3 * 66 * 4
     assert lib.gptoss_attn_decode_workspace_size(2, 64, 0, 0) == 0
 
