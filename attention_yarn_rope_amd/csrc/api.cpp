@@ -228,6 +228,9 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
   if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  // a 64-key tile of K or V must span less than 2 GiB (32-bit buffer offsets)
+  if (k_strides[1] * 2 * 64 > (int64_t)INT32_MAX || v_strides[1] * 2 * 64 > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "token strides of k and v must be below 2^24 elements");
   st = check_table(table, table_rows, rotary_dim, desc_max_len(desc));
   if (st != GPTOSS_OK) return st;
   const size_t need = gptoss_attn_prefill_workspace_size(desc);

@@ -139,6 +139,23 @@ __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
 
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, the gfx9 word 3).
+// A buffer load whose offset lies past `bytes` returns zeros instead of reading.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes < 0 ? 0 : bytes, 0x00020000);
+}
+// 16-byte buffer loads: cached, and non-temporal (buffer_load_dwordx4 ... nt) for read-once data
+__device__ __forceinline__ uint4 ldb16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ldb16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(bf16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

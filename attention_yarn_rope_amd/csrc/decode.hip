@@ -44,18 +44,6 @@ __device__ __forceinline__ float col_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Buffer resource over `bytes` bytes from `base` (raw, stride 0; the gfx9 word 3).
-// A buffer load whose offset lies past `bytes` returns zeros instead of reading.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-// 16-byte non-temporal buffer load (buffer_load_dwordx4 ... nt): read-once data
-__device__ __forceinline__ uint4 ldb16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 template <bool ROTQ>
 __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[NW][SUB * DVS];

@@ -34,7 +34,6 @@ namespace {
 
 constexpr int BQ = kPrefillBQ;  // 32 query positions per item
 constexpr int NK = 64;          // keys per KV tile
-constexpr int NT = 256;         // threads per work group (4 waves)
 constexpr int KS = 72;          // LDS row stride of the K tile (144 B): conflict-free 16 B reads
 constexpr int VS = 80;          // LDS row stride of the V tile (160 B): conflict-free tr16 reads
 constexpr float kSumLimit = 0x1p100f;   // bound of a tile's partial row sum before the reference moves
@@ -51,9 +50,22 @@ __device__ __forceinline__ float wave_xor_sum(float v) {
   return v;
 }
 
-template <bool ROTQ, bool ROTK, bool THD>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+// CB = 16-column blocks per wave: 4 (2 heads x 32 positions, 4 waves of up to
+// 256 VGPRs, 2 per SIMD) or 2 (1 head x 32 positions, 8 waves of up to 128
+// VGPRs, 4 per SIMD: twice the waves to hide latency, for short work items).
+template <int CB> struct Shape {
+  static constexpr int kWaves = 16 / CB;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kThreadsPerRow = kThreads / NK;   // threads staging one 128-byte K/V row
+  static constexpr int kChunks = 8 / kThreadsPerRow;     // 16-byte chunks per thread: 2 or 1
+  static constexpr int kWavesPerEU = CB == 4 ? 2 : 4;
+};
+
+template <bool ROTQ, bool ROTK, bool THD, int CB>
+__global__ __launch_bounds__(Shape<CB>::kThreads) __attribute__((amdgpu_waves_per_eu(Shape<CB>::kWavesPerEU)))
 void prefill_kernel(PrefillParams p) {
+  static_assert(CB == 4 || (CB == 2 && !ROTK), "the fused K rotation needs both halves of a row in one thread");
+  using SH = Shape<CB>;
   __shared__ __attribute__((aligned(16))) bf16_t lds_k[2][NK * KS];
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[2][NK * VS];
 
@@ -99,25 +111,27 @@ void prefill_kernel(PrefillParams p) {
   const int ntiles = (kv_hi - kv_lo + NK - 1) / NK;
   const float sl = p.scale_log2;
 
-  // ---- K/V tile staging: thread -> (row, 8-dim chunk cc and cc + 4). Rows
-  // past the item's last key re-read that key: they lie after every query of
-  // the item, so the causal mask gives them weight exactly 0. ----
-  const int srow = tid >> 2;
-  const int scc = tid & 3;
-  const bf16_t* k_first = p.k + bb_off_k + (int64_t)(ts + kv_lo + srow) * p.k_st + (int64_t)g * p.k_sh + 8 * scc;
-  const bf16_t* v_first = p.v + bb_off_v + (int64_t)(ts + kv_lo + srow) * p.v_st + (int64_t)g * p.v_sh + 8 * scc;
-  const bf16_t* k_last = p.k + bb_off_k + (int64_t)(ts + kv_hi - 1) * p.k_st + (int64_t)g * p.k_sh + 8 * scc;
-  const bf16_t* v_last = p.v + bb_off_v + (int64_t)(ts + kv_hi - 1) * p.v_st + (int64_t)g * p.v_sh + 8 * scc;
-  const int64_t k_step = (int64_t)NK * p.k_st, v_step = (int64_t)NK * p.v_st;
+  // ---- K/V tile staging: thread -> (row, 8-dim chunk cc and cc + 4), read
+  // with raw buffer loads: a uniform base per tile in scalar registers, one
+  // 32-bit per-lane offset, and a range that ends after the item's last key,
+  // so rows past it read as zeros (they lie after every query of the item; the
+  // causal mask gives them weight 0). ----
+  const int srow = tid / SH::kThreadsPerRow;
+  const int scc = tid % SH::kThreadsPerRow;   // chunks scc (and scc + 4 when a thread stages two)
+  const int32_t krow_b = (int32_t)p.k_st * 2, vrow_b = (int32_t)p.v_st * 2;   // row bytes (< 2^31 / 64: host check)
+  const char* k_tile0 = reinterpret_cast<const char*>(p.k + bb_off_k + (int64_t)(ts + kv_lo) * p.k_st + (int64_t)g * p.k_sh);
+  const char* v_tile0 = reinterpret_cast<const char*>(p.v + bb_off_v + (int64_t)(ts + kv_lo) * p.v_st + (int64_t)g * p.v_sh);
+  const uint32_t koff = (uint32_t)(srow * krow_b + 16 * scc);
+  const uint32_t voff = (uint32_t)(srow * vrow_b + 16 * scc);
   uint4 sk1, sk2, sv1, sv2, sc, ss;
   auto load_tile = [&](int t) {
-    const int kpos = kv_lo + t * NK + srow;
-    const bool in = kpos < kv_hi;
-    const bf16_t* kp = in ? k_first + t * k_step : k_last;
-    const bf16_t* vp = in ? v_first + t * v_step : v_last;
-    sk1 = ldg16(kp); sk2 = ldg16(kp + 32);
-    sv1 = ldg16(vp); sv2 = ldg16(vp + 32);
+    const int rows = kv_hi - (kv_lo + t * NK);   // keys of the item from this tile on (>= 1)
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_tile0 + (int64_t)t * NK * krow_b, (rows - 1) * krow_b + 2 * kHeadDim);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_tile0 + (int64_t)t * NK * vrow_b, (rows - 1) * vrow_b + 2 * kHeadDim);
+    sk1 = ldb16(rk, koff); sv1 = ldb16(rv, voff);
+    if (SH::kChunks == 2) { sk2 = ldb16(rk, koff + 64); sv2 = ldb16(rv, voff + 64); }
     if (ROTK) {
+      const int kpos = kv_lo + t * NK + srow;
       const bf16_t* tp = p.table + (int64_t)min(min(kpos, kv_hi - 1), p.table_rows - 1) * kHeadDim + 8 * scc;
       sc = ldg16(tp); ss = ldg16(tp + 32);
     }
@@ -128,9 +142,11 @@ void prefill_kernel(PrefillParams p) {
     bf16_t* kd = &lds_k[buf][srow * KS + 8 * scc];
     bf16_t* vd = &lds_v[buf][srow * VS + 8 * scc];
     *reinterpret_cast<uint4*>(kd) = k1;
-    *reinterpret_cast<uint4*>(kd + 32) = k2;
     *reinterpret_cast<uint4*>(vd) = sv1;
-    *reinterpret_cast<uint4*>(vd + 32) = sv2;
+    if (SH::kChunks == 2) {
+      *reinterpret_cast<uint4*>(kd + 32) = k2;
+      *reinterpret_cast<uint4*>(vd + 32) = sv2;
+    }
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load. Every
@@ -138,15 +154,15 @@ void prefill_kernel(PrefillParams p) {
   // any of them is used, so the work item pays one memory latency, not several.
   // Rows past the end load a valid row and are never stored. ----
   if (ntiles > 0) load_tile(0);
-  bf16x8_t qf[4][2];
+  bf16x8_t qf[CB][2];
   int qpos[2];
   qpos[0] = q0 + col;
   qpos[1] = q0 + 16 + col;
-  uint4 qx[4][2], qt[4][2];
-  float sink_raw[4];
+  uint4 qx[CB][2], qt[CB][2];
+  float sink_raw[CB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int head = g * kGroup + wave * 2 + (cb >> 1);
+  for (int cb = 0; cb < CB; ++cb) {
+    const int head = g * kGroup + wave * (CB / 2) + (cb >> 1);
     const int pos = min(qpos[cb & 1], qlast);
     const bf16_t* qp = p.q + bb_off_q + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh;
     qx[cb][0] = ldg16(qp + 8 * grp);
@@ -158,9 +174,9 @@ void prefill_kernel(PrefillParams p) {
     }
     sink_raw[cb] = __ldg(p.sinks + head);
   }
-  float ref[4], lsum[4];
+  float ref[CB], lsum[CB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     uint4 y1 = qx[cb][0], y2 = qx[cb][1];
     if (ROTQ) rope8(qx[cb][0], qx[cb][1], qt[cb][0], qt[cb][1], y1, y2);
     qf[cb][0] = as_bf16x8(y1);
@@ -173,7 +189,7 @@ void prefill_kernel(PrefillParams p) {
     lsum[cb] = (grp == 0 && has_sink) ? 1.0f : 0.0f;
   }
 
-  f32x4_t oacc[4][4];  // [d block][column block]
+  f32x4_t oacc[4][CB];  // [d block][column block]
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -190,14 +206,14 @@ void prefill_kernel(PrefillParams p) {
     const bf16_t* vt = lds_v[buf];
 
     // ---- S^T = K Q^T: sacc[kb][cb] element r = key (kb*16 + 4*grp + r), query col ----
-    f32x4_t sacc[4][4];
+    f32x4_t sacc[4][CB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const bf16_t* krow = kt + (kb * 16 + col) * KS + 8 * grp;
       const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(krow));
       const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32));
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         z = mfma16(a0, qf[cb][0], z);
         sacc[kb][cb] = mfma16(a1, qf[cb][1], z);
@@ -216,7 +232,7 @@ void prefill_kernel(PrefillParams p) {
           const bool vis0 = (uint32_t)(qpos[0] - kpos) < weff;
           const bool vis1 = (uint32_t)(qpos[1] - kpos) < weff;
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
+          for (int cb = 0; cb < CB; ++cb) {
             const bool vis = (cb & 1) ? vis1 : vis0;
             sacc[kb][cb][r] = vis ? sacc[kb][cb][r] : -INFINITY;
           }
@@ -230,8 +246,8 @@ void prefill_kernel(PrefillParams p) {
     // becomes the reference, l and O are rescaled and the tile is redone. Values
     // below or above the reference by up to 2^100 lose no relative precision in
     // fp32 / bf16, so the result is the same ratio as with a running max.
-    bf16x8_t pf[4][2];
-    float tsum[4];
+    bf16x8_t pf[CB][2];
+    float tsum[CB];
     bool bad = false;
     auto exp_tile = [&](int cb) {
       uint32_t w[8];
@@ -253,13 +269,13 @@ void prefill_kernel(PrefillParams p) {
       pf[cb][1] = __builtin_bit_cast(bf16x8_t, make_uint4(w[4], w[5], w[6], w[7]));
     };
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       exp_tile(cb);
       bad |= !(tsum[cb] <= kSumLimit);
     }
     if (__any(bad)) {   // rare, wave-uniform
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         float v = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -277,7 +293,7 @@ void prefill_kernel(PrefillParams p) {
       }
     }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) lsum[cb] += tsum[cb];
+    for (int cb = 0; cb < CB; ++cb) lsum[cb] += tsum[cb];
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -289,7 +305,7 @@ void prefill_kernel(PrefillParams p) {
         const uint2 hi = lds_read_tr16(vb + 16 * VS);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) oacc[db][cb] = mfma16(a, pf[cb][ks], oacc[db][cb]);
+        for (int cb = 0; cb < CB; ++cb) oacc[db][cb] = mfma16(a, pf[cb][ks], oacc[db][cb]);
       }
     }
 
@@ -299,12 +315,12 @@ void prefill_kernel(PrefillParams p) {
 
   // ---- epilogue: o = acc / l, bf16 store; lane holds d = 16*db + 4*grp + r ----
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     const float l = wave_xor_sum(lsum[cb]);
     const int pos = qpos[cb & 1];
     if (pos > qlast) continue;
     const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
-    const int head = g * kGroup + wave * 2 + (cb >> 1);
+    const int head = g * kGroup + wave * (CB / 2) + (cb >> 1);
     bf16_t* op = p.o + bb_off_o + (int64_t)(ts + pos) * p.o_st + (int64_t)head * p.o_sh + 4 * grp;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -385,7 +401,16 @@ template <bool ROTQ, bool ROTK, bool THD>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.q_blocks * (THD ? 1 : p.batch) * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD>), dim3((uint32_t)blocks), dim3(NT), 0, stream, p);
+  // short work items (window layers): twice the waves per SIMD to hide their load latency
+  if constexpr (!ROTK) {
+    if (p.window > 0) {
+      hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD, 2>), dim3((uint32_t)blocks), dim3(Shape<2>::kThreads), 0,
+                         stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD, 4>), dim3((uint32_t)blocks), dim3(Shape<4>::kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
