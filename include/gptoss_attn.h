@@ -166,6 +166,9 @@ gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc,
  *            bytes, 256-byte aligned; its content need not be initialised.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads). A row with no
  * visible key (only possible for empty sequences) writes nothing.
+ * The token strides of k and v must be below 2^24 elements (64 rows of a key
+ * tile are addressed with 32-bit byte offsets); larger ones return
+ * GPTOSS_ERR_UNSUPPORTED.
  */
 size_t gptoss_attn_prefill_workspace_size(const gptoss_seq_desc* desc);
 gptoss_status gptoss_attn_prefill(const gptoss_seq_desc* desc,
@@ -212,9 +215,15 @@ gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc,
  *             or the last min(L_n, W) of them on a window layer.
  *   out:      bf16 [N, Hq, D], o_strides[2].
  *   num_splits: key chunks per sequence processed in parallel and merged
- *             (0 = choose automatically); results agree up to fp32
- *             reassociation for any value.
- *   workspace: >= gptoss_attn_decode_workspace_size(...) bytes.
+ *             (0 = choose automatically: a small planning kernel reads the
+ *             cache lengths and sizes the chunks for the device); results
+ *             agree up to fp32 reassociation for any value.
+ *   workspace: >= gptoss_attn_decode_workspace_size(...) bytes, 256-byte
+ *             aligned: partial results and the chunk plan; its content need
+ *             not be initialised.
+ * kv_strides[1] must be >= 64 and max_cache_len * kv_strides[1] * 2 bytes below
+ * 2^31 (one sequence's rows are read through a 32-bit buffer range); other
+ * values return GPTOSS_ERR_UNSUPPORTED.
  */
 size_t gptoss_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                          int32_t max_cache_len, int32_t num_splits);
