@@ -12,10 +12,11 @@
 //
 // Work item: (sequence, KV head g, block of BQ = 32 query positions). Its 256
 // query rows are the 8 heads of group g x 32 positions, so every K/V tile is
-// read from HBM once and staged in LDS once for the whole GQA group. Each of the
-// 4 waves owns 64 query rows (2 heads x 32 positions) as four 16-column blocks.
-// Per KV tile of 64 keys a wave runs 32 MFMAs for S^T = K Q^T and 32 for
-// O^T = V^T P^T (v_mfma_f32_16x16x32_bf16, fp32 accumulation). The softmax
+// read from HBM once and staged in LDS once for the whole GQA group. Each of
+// 4 waves owns 64 query rows (2 heads x 32 positions) as four 16-column blocks
+// (CB = 4; window layers use 8 waves of 32 rows, CB = 2). Per KV tile of 64
+// keys a CB = 4 wave runs 32 MFMAs for S^T = K Q^T and 32 for O^T = V^T P^T
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation). The softmax
 // runs on S^T, whose accumulator layout is already the B-operand layout P^T
 // needs (keys permuted consistently between V^T and P^T). V^T comes straight
 // from the row-major V tile in LDS through ds_read_b64_tr_b16.
