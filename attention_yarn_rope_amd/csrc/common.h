@@ -38,6 +38,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // above the midpoint by the sign of the fma's rounding error e (found with
 // the TwoSum error-free transformation). The result equals the exact value
 // rounded once to bf16 (nearest-even).
+//
+// The fix-up only runs where it can matter. Write y = p - t with p and t the
+// two exact products. Each is an integer multiple of 2^(E - 15), E its binary
+// exponent, so y is a multiple of 2^(min(Ep, Et) - 15) and fits in fp32's 24
+// bits unless its exponent reaches min(Ep, Et) + 9. An inexact result s
+// therefore has min(|p|, |t|) < 2^(Es - 8) <= |s| * 2^-8. Outputs on a bf16
+// midpoint that fail this test are exact (the common case: exact results often
+// end in zero bits) and need no fix; with random bf16 data the test leaves
+// about one wave in a hundred on the slow path instead of nearly all of them.
 // ---------------------------------------------------------------------------
 #pragma clang fp contract(off)
 __device__ __forceinline__ float two_sum_err(float a, float b, float s) {
@@ -55,8 +64,12 @@ __device__ __forceinline__ float fix_bf16_tie(float a, float b, float s) {
   return __uint_as_float(((u & 0xFFFFu) == 0x8000u) ? u + step : u);
 }
 
-// 0 exactly when the fp32 value's low 16 bits are 0x8000 (a bf16 midpoint)
-__device__ __forceinline__ uint32_t midpoint_key(float v) { return (__float_as_uint(v) << 16) ^ 0x80000000u; }
+// s = RN_fp32(p + t) with p, t exact products of bf16 values: true when s lies
+// on a bf16 midpoint (low 16 bits 0x8000) and may be inexact (see above).
+__device__ __forceinline__ bool maybe_inexact_tie(float s, float p, float t) {
+  return ((__float_as_uint(s) & 0xFFFFu) == 0x8000u) &&
+         (__builtin_fminf(__builtin_fabsf(p), __builtin_fabsf(t)) < __builtin_fabsf(s) * 0x1p-8f);
+}
 
 // Rotate 8 pairs: x1 holds dims i..i+7, x2 dims i+32..i+39 (rotary_dim 64),
 // c / s the table's cos / sin for the same i. Writes rounded bf16 outputs.
@@ -69,7 +82,7 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
   uint32_t* py1 = reinterpret_cast<uint32_t*>(&y1);
   uint32_t* py2 = reinterpret_cast<uint32_t*>(&y2);
   float r1[8], r2[8];
-  uint32_t key = 0xFFFFFFFFu;   // min over the outputs of midpoint_key: 0 iff any sits on a midpoint
+  bool fix = false;   // some output may be an inexact result on a bf16 midpoint
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
 #pragma unroll
@@ -78,16 +91,16 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
       float a2 = h ? bf16_hi(px2[w]) : bf16_lo(px2[w]);
       float cc = h ? bf16_hi(pc[w]) : bf16_lo(pc[w]);
       float ss = h ? bf16_hi(ps[w]) : bf16_lo(ps[w]);
-      float t1 = a2 * ss;                      // exact
-      float t2 = a1 * ss;                      // exact
-      float o1 = __builtin_fmaf(a1, cc, -t1);  // RN(x1*C - x2*S)
-      float o2 = __builtin_fmaf(a2, cc, t2);   // RN(x2*C + x1*S)
+      float p1 = a1 * cc, t1 = a2 * ss;        // exact
+      float p2 = a2 * cc, t2 = a1 * ss;        // exact
+      float o1 = p1 - t1;                      // RN(x1*C - x2*S)
+      float o2 = p2 + t2;                      // RN(x2*C + x1*S)
       r1[2 * w + h] = o1;
       r2[2 * w + h] = o2;
-      key = min(key, min(midpoint_key(o1), midpoint_key(o2)));
+      fix |= maybe_inexact_tie(o1, p1, t1) | maybe_inexact_tie(o2, p2, t2);
     }
   }
-  if (key == 0u) {  // rare: redo every element with the exact fix-up (a no-op off midpoints)
+  if (fix) {  // rare: redo every element with the exact fix-up (a no-op where not needed)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
 #pragma unroll

@@ -62,13 +62,21 @@ template <int CB> struct Shape {
   static constexpr int kWavesPerEU = CB == 4 ? 2 : 4;
 };
 
-template <bool ROTQ, bool ROTK, bool THD, int CB>
+// Staging: ALL = false streams the item's key tiles through two LDS buffers,
+// loading tile t + 1 while tile t is computed. ALL = true (short windows: at
+// most kAllTiles tiles per item) loads every tile in the prologue, together
+// with q, so the item waits for memory once and then runs its tiles with no
+// further loads or barriers.
+constexpr int kAllTiles = 3;
+
+template <bool ROTQ, bool ROTK, bool THD, int CB, bool ALL>
 __global__ __launch_bounds__(Shape<CB>::kThreads) __attribute__((amdgpu_waves_per_eu(Shape<CB>::kWavesPerEU)))
 void prefill_kernel(PrefillParams p) {
   static_assert(CB == 4 || (CB == 2 && !ROTK), "the fused K rotation needs both halves of a row in one thread");
   using SH = Shape<CB>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_k[2][NK * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_v[2][NK * VS];
+  constexpr int NBUF = ALL ? kAllTiles : 2;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_k[NBUF][NK * KS];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_v[NBUF][NK * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,37 +132,46 @@ void prefill_kernel(PrefillParams p) {
   const char* v_tile0 = reinterpret_cast<const char*>(p.v + bb_off_v + (int64_t)(ts + kv_lo) * p.v_st + (int64_t)g * p.v_sh);
   const uint32_t koff = (uint32_t)(srow * krow_b + 16 * scc);
   const uint32_t voff = (uint32_t)(srow * vrow_b + 16 * scc);
-  uint4 sk1, sk2, sv1, sv2, sc, ss;
-  auto load_tile = [&](int t) {
-    const int rows = kv_hi - (kv_lo + t * NK);   // keys of the item from this tile on (>= 1)
+  // A tile past the item's last one gets an empty range: its loads return
+  // zeros without touching memory.
+  struct Stage { uint4 k1, k2, v1, v2, c, s; };
+  auto load_tile = [&](int t, Stage& st) {
+    const int rows = kv_hi - (kv_lo + t * NK);   // keys of the item from this tile on
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_tile0 + (int64_t)t * NK * krow_b, (rows - 1) * krow_b + 2 * kHeadDim);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_tile0 + (int64_t)t * NK * vrow_b, (rows - 1) * vrow_b + 2 * kHeadDim);
-    sk1 = ldb16(rk, koff); sv1 = ldb16(rv, voff);
-    if (SH::kChunks == 2) { sk2 = ldb16(rk, koff + 64); sv2 = ldb16(rv, voff + 64); }
+    st.k1 = ldb16(rk, koff); st.v1 = ldb16(rv, voff);
+    if (SH::kChunks == 2) { st.k2 = ldb16(rk, koff + 64); st.v2 = ldb16(rv, voff + 64); }
     if (ROTK) {
       const int kpos = kv_lo + t * NK + srow;
       const bf16_t* tp = p.table + (int64_t)min(min(kpos, kv_hi - 1), p.table_rows - 1) * kHeadDim + 8 * scc;
-      sc = ldg16(tp); ss = ldg16(tp + 32);
+      st.c = ldg16(tp); st.s = ldg16(tp + 32);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint4 k1 = sk1, k2 = sk2;
-    if (ROTK) rope8(sk1, sk2, sc, ss, k1, k2);
+  auto store_tile = [&](int buf, const Stage& st) {
+    uint4 k1 = st.k1, k2 = st.k2;
+    if (ROTK) rope8(st.k1, st.k2, st.c, st.s, k1, k2);
     bf16_t* kd = &lds_k[buf][srow * KS + 8 * scc];
     bf16_t* vd = &lds_v[buf][srow * VS + 8 * scc];
     *reinterpret_cast<uint4*>(kd) = k1;
-    *reinterpret_cast<uint4*>(vd) = sv1;
+    *reinterpret_cast<uint4*>(vd) = st.v1;
     if (SH::kChunks == 2) {
       *reinterpret_cast<uint4*>(kd + 32) = k2;
-      *reinterpret_cast<uint4*>(vd + 32) = sv2;
+      *reinterpret_cast<uint4*>(vd + 32) = st.v2;
     }
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load. Every
-  // independent load (the first K/V tile, q, table rows, sinks) is issued before
-  // any of them is used, so the work item pays one memory latency, not several.
-  // Rows past the end load a valid row and are never stored. ----
-  if (ntiles > 0) load_tile(0);
+  // independent load (the first K/V tile or, with ALL, every tile; q, table
+  // rows, sinks) is issued before any of them is used, so the work item pays
+  // one memory latency, not several. Rows past the end load a valid row and are
+  // never stored. ----
+  Stage st[ALL ? kAllTiles : 1];
+  if (ALL) {
+#pragma unroll
+    for (int t = 0; t < kAllTiles; ++t) load_tile(t, st[t]);
+  } else if (ntiles > 0) {
+    load_tile(0, st[0]);
+  }
   bf16x8_t qf[CB][2];
   int qpos[2];
   qpos[0] = q0 + col;
@@ -196,12 +213,17 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) oacc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (ntiles > 0) store_tile(0);
+  if (ALL) {
+#pragma unroll
+    for (int t = 0; t < kAllTiles; ++t) store_tile(t, st[t]);
+  } else if (ntiles > 0) {
+    store_tile(0, st[0]);
+  }
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    const int buf = ALL ? t : (t & 1);
+    if (!ALL && t + 1 < ntiles) load_tile(t + 1, st[0]);
     const int tile0 = kv_lo + t * NK;
     const bf16_t* kt = lds_k[buf];
     const bf16_t* vt = lds_v[buf];
@@ -310,8 +332,10 @@ void prefill_kernel(PrefillParams p) {
       }
     }
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    if (!ALL) {
+      if (t + 1 < ntiles) store_tile(buf ^ 1, st[0]);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: o = acc / l, bf16 store; lane holds d = 16*db + 4*grp + r ----
@@ -402,15 +426,21 @@ template <bool ROTQ, bool ROTK, bool THD>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.q_blocks * (THD ? 1 : p.batch) * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  // short work items (window layers): twice the waves per SIMD to hide their load latency
+  // short work items (window layers): twice the waves per SIMD to hide their
+  // load latency; windows whose items span at most kAllTiles key tiles
+  // (window + BQ - 1 keys at most) stage all of them at once.
   if constexpr (!ROTK) {
     if (p.window > 0) {
-      hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD, 2>), dim3((uint32_t)blocks), dim3(Shape<2>::kThreads), 0,
-                         stream, p);
+      if (p.window + BQ - 1 <= kAllTiles * NK)
+        hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD, 2, true>), dim3((uint32_t)blocks),
+                           dim3(Shape<2>::kThreads), 0, stream, p);
+      else
+        hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD, 2, false>), dim3((uint32_t)blocks),
+                           dim3(Shape<2>::kThreads), 0, stream, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD, 4>), dim3((uint32_t)blocks), dim3(Shape<4>::kThreads), 0,
+  hipLaunchKernelGGL((prefill_kernel<ROTQ, ROTK, THD, 4, false>), dim3((uint32_t)blocks), dim3(Shape<4>::kThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
