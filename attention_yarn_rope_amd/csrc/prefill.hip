@@ -62,6 +62,8 @@ template <int CB> struct Shape {
   static constexpr int kWavesPerEU = CB == 4 ? 2 : 4;
 };
 
+template <int N> struct KeyCount { static constexpr int value = N; };   // keys per compute step
+
 // Staging: ALL = false streams the item's key tiles through two LDS buffers,
 // loading tile t + 1 while tile t is computed. ALL = true (short windows: at
 // most kAllTiles tiles per item) loads every tile in the prologue, together
@@ -75,8 +77,8 @@ void prefill_kernel(PrefillParams p) {
   static_assert(CB == 4 || (CB == 2 && !ROTK), "the fused K rotation needs both halves of a row in one thread");
   using SH = Shape<CB>;
   constexpr int NBUF = ALL ? kAllTiles : 2;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_k[NBUF][NK * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_v[NBUF][NK * VS];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_k[NBUF * NK * KS];   // tile b at b * NK * KS
+  __shared__ __attribute__((aligned(16))) bf16_t lds_v[NBUF * NK * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,8 +152,8 @@ void prefill_kernel(PrefillParams p) {
   auto store_tile = [&](int buf, const Stage& st) {
     uint4 k1 = st.k1, k2 = st.k2;
     if (ROTK) rope8(st.k1, st.k2, st.c, st.s, k1, k2);
-    bf16_t* kd = &lds_k[buf][srow * KS + 8 * scc];
-    bf16_t* vd = &lds_v[buf][srow * VS + 8 * scc];
+    bf16_t* kd = lds_k + buf * NK * KS + srow * KS + 8 * scc;
+    bf16_t* vd = lds_v + buf * NK * VS + srow * VS + 8 * scc;
     *reinterpret_cast<uint4*>(kd) = k1;
     *reinterpret_cast<uint4*>(vd) = st.v1;
     if (SH::kChunks == 2) {
@@ -211,7 +213,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) oacc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < CB; ++b) oacc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (ALL) {
 #pragma unroll
@@ -221,17 +223,17 @@ void prefill_kernel(PrefillParams p) {
   }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = ALL ? t : (t & 1);
-    if (!ALL && t + 1 < ntiles) load_tile(t + 1, st[0]);
-    const int tile0 = kv_lo + t * NK;
-    const bf16_t* kt = lds_k[buf];
-    const bf16_t* vt = lds_v[buf];
+  // ---- one compute step over NKT keys (64: a whole tile, 32: half of one) whose
+  // K and V rows start at kt and vt in LDS; tile0 = position of the first key ----
+  auto compute = [&](auto nkt_tag, const bf16_t* kt, const bf16_t* vt, int tile0) __attribute__((always_inline)) {
+    constexpr int NKT = decltype(nkt_tag)::value;
+    constexpr int KBN = NKT / 16;   // 16-key blocks of S^T
+    constexpr int KSN = NKT / 32;   // 32-key slices of P^T (one PV MFMA each)
 
     // ---- S^T = K Q^T: sacc[kb][cb] element r = key (kb*16 + 4*grp + r), query col ----
-    f32x4_t sacc[4][CB];
+    f32x4_t sacc[KBN][CB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KBN; ++kb) {
       const bf16_t* krow = kt + (kb * 16 + col) * KS + 8 * grp;
       const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(krow));
       const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32));
@@ -243,12 +245,12 @@ void prefill_kernel(PrefillParams p) {
       }
     }
 
-    // ---- mask: only tiles that are not fully visible to every query of the item.
+    // ---- mask: only steps that are not fully visible to every query of the item.
     // visible <=> 0 <= qpos - kpos < weff, one unsigned compare (branch free) ----
-    const bool full = (tile0 + NK - 1 <= q0) && (W == 0 || qlast - tile0 < W);
+    const bool full = (tile0 + NKT - 1 <= q0) && (W == 0 || qlast - tile0 < W);
     if (!full) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int kpos = tile0 + kb * 16 + 4 * grp + r;
@@ -264,19 +266,19 @@ void prefill_kernel(PrefillParams p) {
 
     // ---- online softmax against a fixed reference (log2 units) ----
     // p = exp2(s*tau*log2(e) - ref). The reference starts at the sink logit and
-    // only moves when a tile's bf16 row sum leaves [0, 2^100] (a score that far
-    // above the reference, or an overflow): then the tile's true column max
-    // becomes the reference, l and O are rescaled and the tile is redone. Values
+    // only moves when a step's bf16 row sum leaves [0, 2^100] (a score that far
+    // above the reference, or an overflow): then the step's true column max
+    // becomes the reference, l and O are rescaled and the step is redone. Values
     // below or above the reference by up to 2^100 lose no relative precision in
     // fp32 / bf16, so the result is the same ratio as with a running max.
-    bf16x8_t pf[CB][2];
+    bf16x8_t pf[CB][KSN];
     float tsum[CB];
     bool bad = false;
-    auto exp_tile = [&](int cb) {
-      uint32_t w[8];
+    auto exp_tile = [&](int cb) __attribute__((always_inline)) {
+      uint32_t w[2 * KBN];
       const float nr = -ref[cb];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KBN; ++kb) {
         w[2 * kb] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][0], sl, nr)),
                                 __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][1], sl, nr)));
         w[2 * kb + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][cb][2], sl, nr)),
@@ -285,11 +287,12 @@ void prefill_kernel(PrefillParams p) {
       // row sum of the bf16-rounded probabilities actually used by PV
       float ts = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ts = add_bf16x2(w[i], ts);
+      for (int i = 0; i < 2 * KBN; ++i) ts = add_bf16x2(w[i], ts);
       tsum[cb] = ts;
-      // keys pi(grp, e): e < 4 -> 4*grp + e of key block 2ks, e >= 4 -> of key block 2ks+1
-      pf[cb][0] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-      pf[cb][1] = __builtin_bit_cast(bf16x8_t, make_uint4(w[4], w[5], w[6], w[7]));
+      // keys pi(grp, e) of slice ks: e < 4 -> 4*grp + e of key block 2ks, e >= 4 -> of key block 2ks+1
+#pragma unroll
+      for (int ks = 0; ks < KSN; ++ks)
+        pf[cb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w[4 * ks], w[4 * ks + 1], w[4 * ks + 2], w[4 * ks + 3]));
     };
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -301,7 +304,7 @@ void prefill_kernel(PrefillParams p) {
       for (int cb = 0; cb < CB; ++cb) {
         float v = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) v = __builtin_fmaxf(v, sacc[kb][cb][r]);
         const float mt = wave_xor_max(v) * sl;     // the column's max (log2 units)
@@ -320,7 +323,7 @@ void prefill_kernel(PrefillParams p) {
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KSN; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const bf16_t* vb = vt + (32 * ks + 4 * grp + (col >> 2)) * VS + 16 * db + 4 * (col & 3);
@@ -331,8 +334,19 @@ void prefill_kernel(PrefillParams p) {
         for (int cb = 0; cb < CB; ++cb) oacc[db][cb] = mfma16(a, pf[cb][ks], oacc[db][cb]);
       }
     }
+  };
 
-    if (!ALL) {
+  if (ALL) {
+    // every tile is in LDS, rows in key order: 32-key steps, and only the steps
+    // holding keys of the item (a 159-key window span takes 5 steps, not 6)
+    const int nsteps = (kv_hi - kv_lo + 31) / 32;
+    for (int u = 0; u < nsteps; ++u)
+      compute(KeyCount<32>(), lds_k + u * 32 * KS, lds_v + u * 32 * VS, kv_lo + 32 * u);
+  } else {
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < ntiles) load_tile(t + 1, st[0]);
+      compute(KeyCount<NK>(), lds_k + buf * NK * KS, lds_v + buf * NK * VS, kv_lo + t * NK);
       if (t + 1 < ntiles) store_tile(buf ^ 1, st[0]);
       __syncthreads();
     }

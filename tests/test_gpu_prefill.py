@@ -53,6 +53,16 @@ def test_bshd_ragged(table, B, S, window):
     assert_close(out, _ref_bshd(inp, window), f"bshd B={B} S={S} W={window}")
 
 
+@pytest.mark.parametrize("window", [161, 162])
+def test_window_staging_boundary(table, window):
+    """W = 161 is the widest window whose 32-query items span at most 3 key
+    tiles (all staged at once); W = 162 needs 4 tiles and streams them."""
+    inp = wl.prefill_bshd(2, 700, seed=400 + window)
+    say(f"[gpu] prefill window staging boundary W={window}")
+    out = _run_bshd(inp, window, table)
+    assert_close(out, _ref_bshd(inp, window), f"bshd B=2 S=700 W={window}")
+
+
 @pytest.mark.parametrize("hkv", [1, 2])
 def test_other_group_counts(table, hkv):
     inp = wl.prefill_bshd(1, 300, seed=300 + hkv, hq=8 * hkv, hkv=hkv)
