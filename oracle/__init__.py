@@ -26,6 +26,10 @@ Sources (the pages are cited by title and section):
   * "gpt-oss-20b 模型结构" (model-structure print-out): q_proj 2880->4096,
     k_proj / v_proj 2880->512, so 64 query heads and 8 KV heads of width 64.
 
+``oracle.backward`` adds the log-sum-exp of each row and the gradients of the
+attention with respect to q, k, v and the sinks: the derivatives of the same
+definition (no page prints a backward pass).
+
 Parity unpinned: agreement with real GPT-OSS checkpoints. The pages print no
 activations or outputs, and the RoPE pairing (half-split) and the YaRN ramp
 shape (linear in the dimension index) are readings of the pages, not facts
@@ -42,10 +46,12 @@ from .attention import (
     prefill_rows,
     decode,
 )
+from .backward import rotate_transpose, sink_attention_backward, prefill_bshd_backward, prefill_thd_backward
 
 __all__ = [
     "round_bf16", "bf16_bits", "from_bf16_bits",
     "RopeConfig", "yarn_params", "cos_sin_table", "freqs_cis",
     "rotate", "rope_qk_bshd", "rope_qk_thd", "thd_positions",
     "sink_attention", "prefill_bshd", "prefill_thd", "prefill_rows", "decode",
+    "rotate_transpose", "sink_attention_backward", "prefill_bshd_backward", "prefill_thd_backward",
 ]
