@@ -1,7 +1,8 @@
 """GPT-OSS attention hot path on MI355X: YaRN RoPE, sink + GQA + sliding-window
-prefill (BSHD and packed THD) and split-KV decode, as hand-written gfx950 HIP
-kernels behind a C ABI (include/gptoss_attn.h). This package is the thin torch
-binding; libgptoss_attn.so is loaded on first use and is required.
+prefill (BSHD and packed THD) with its backward pass, and split-KV decode, as
+hand-written gfx950 HIP kernels behind a C ABI (include/gptoss_attn.h). This
+package is the thin torch binding; libgptoss_attn.so is loaded on first use and
+is required.
 """
 
 from .api import (  # noqa: F401
@@ -10,8 +11,11 @@ from .api import (  # noqa: F401
     rope_table,
     rope_qk,
     attn_prefill,
+    attn_prefill_lse,
+    attn_prefill_backward,
     attn_decode,
     prefill_workspace_size,
+    prefill_backward_workspace_size,
     decode_workspace_size,
 )
 from ._lib import GptossError, load as load_library  # noqa: F401

@@ -47,6 +47,14 @@ SIGNATURES = {
     "gptoss_attn_prefill_ex": (ctypes.c_int, [ctypes.POINTER(SeqDesc), c_vp, I64x3, c_vp, I64x3, c_vp, I64x3,
                                               c_vp, c_f32, c_i32, c_vp, c_i32, c_i32, c_vp, I64x3,
                                               c_vp, c_size, c_i32, c_vp]),
+    "gptoss_attn_prefill_lse": (ctypes.c_int, [ctypes.POINTER(SeqDesc), c_vp, I64x3, c_vp, I64x3, c_vp, I64x3,
+                                               c_vp, c_f32, c_i32, c_vp, c_i32, c_i32, c_vp, I64x3, c_vp,
+                                               c_vp, c_size, c_vp]),
+    "gptoss_attn_prefill_backward_workspace_size": (c_size, [ctypes.POINTER(SeqDesc)]),
+    "gptoss_attn_prefill_backward": (ctypes.c_int, [ctypes.POINTER(SeqDesc), c_vp, I64x3, c_vp, I64x3, c_vp, I64x3,
+                                                    c_vp, c_f32, c_i32, c_vp, c_i32, c_i32, c_vp, I64x3,
+                                                    c_vp, I64x3, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                    c_vp, c_size, c_vp]),
     "gptoss_attn_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
     "gptoss_attn_decode": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, I64x2, c_vp, c_vp, I64x3,
                                           c_vp, c_i32, c_vp, c_f32, c_i32, c_vp, c_i32, c_i32, c_vp, I64x2,

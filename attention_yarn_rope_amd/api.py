@@ -130,6 +130,77 @@ def attn_prefill(q, k, v, sinks, window=0, table=None, softmax_scale=None, cu_se
     return out
 
 
+def _sinks(sinks):
+    if sinks.dtype != torch.float32 or not sinks.is_cuda or not sinks.is_contiguous():
+        raise TypeError("sinks must be a contiguous CUDA float32 tensor")
+    return sinks
+
+
+def attn_prefill_lse(q, k, v, sinks, window=0, table=None, softmax_scale=None, cu_seqlens=None, max_seqlen=None,
+                     out=None, lse=None, workspace=None):
+    """attn_prefill that also returns each row's log-sum-exp: (out, lse fp32 [tokens, Hq])."""
+    _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _sinks(sinks)
+    desc, layout = _desc(q, k, cu_seqlens, max_seqlen)
+    tokens = q.shape[0] * q.shape[1] if layout == _lib.BSHD else q.shape[0]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((tokens, q.shape[-2]), dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != tokens * q.shape[-2]:
+        raise ValueError("lse must be a contiguous float32 [tokens, Hq] tensor")
+    _bf16(out, "out")
+    lib = _lib.load()
+    need = lib.gptoss_attn_prefill_workspace_size(ctypes.byref(desc))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    check("gptoss_attn_prefill_lse", lib.gptoss_attn_prefill_lse(
+        ctypes.byref(desc), _ptr(q), _strides3(q, layout), _ptr(k), _strides3(k, layout),
+        _ptr(v), _strides3(v, layout), _ptr(sinks), float(scale), int(window), tptr, trows, tdim,
+        _ptr(out), _strides3(out, layout), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
+
+
+def prefill_backward_workspace_size(q, k, cu_seqlens=None, max_seqlen=None):
+    desc, _ = _desc(q, k, cu_seqlens, max_seqlen)
+    return _lib.load().gptoss_attn_prefill_backward_workspace_size(ctypes.byref(desc))
+
+
+def attn_prefill_backward(q, k, v, sinks, out, dout, lse, window=0, table=None, softmax_scale=None,
+                          cu_seqlens=None, max_seqlen=None, workspace=None, grads=None):
+    """Gradients of attn_prefill: (dq, dk, dv bf16 contiguous in q/k/v's layout, dsinks fp32 [Hq]).
+
+    q, k, v, sinks, window, table, softmax_scale as given to the forward; out and lse
+    from attn_prefill_lse; dout = dL/d out. ``grads`` may pass preallocated (dq, dk, dv, dsinks).
+    """
+    _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(out, "out"), _bf16(dout, "dout"), _sinks(sinks)
+    desc, layout = _desc(q, k, cu_seqlens, max_seqlen)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    if grads is None:
+        grads = (torch.empty(q.shape, dtype=torch.bfloat16, device=q.device),
+                 torch.empty(k.shape, dtype=torch.bfloat16, device=q.device),
+                 torch.empty(v.shape, dtype=torch.bfloat16, device=q.device),
+                 torch.empty(q.shape[-2], dtype=torch.float32, device=q.device))
+    dq, dk, dv, dsinks = grads
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t.shape != ref.shape or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like its input")
+    lib = _lib.load()
+    need = lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(desc))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    check("gptoss_attn_prefill_backward", lib.gptoss_attn_prefill_backward(
+        ctypes.byref(desc), _ptr(q), _strides3(q, layout), _ptr(k), _strides3(k, layout),
+        _ptr(v), _strides3(v, layout), _ptr(sinks), float(scale), int(window), tptr, trows, tdim,
+        _ptr(out), _strides3(out, layout), _ptr(dout), _strides3(dout, layout), _ptr(lse),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv, dsinks
+
+
 def decode_workspace_size(num_seqs, num_q_heads, max_cache_len, num_splits=0):
     return _lib.load().gptoss_attn_decode_workspace_size(num_seqs, num_q_heads, max_cache_len, num_splits)
 

@@ -215,8 +215,8 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
                            const void* k, const int64_t k_strides[3], const void* v,
                            const int64_t v_strides[3], const float* sinks, float softmax_scale,
                            int32_t window, const void* table, int32_t table_rows, int32_t rotary_dim,
-                           void* out, const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
-                           int krot, void* stream) {
+                           void* out, const int64_t o_strides[3], float* lse, void* workspace,
+                           size_t workspace_bytes, int krot, void* stream) {
   gptoss_status st = check_desc(desc);
   if (st != GPTOSS_OK) return st;
   if (desc_tokens(desc) == 0 || desc->batch == 0) return GPTOSS_OK;
@@ -261,6 +261,7 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
   p.window = window;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
+  p.lse = lse;
 
   if (thd) {
     const int32_t max_items = thd_max_items(desc);
@@ -316,7 +317,19 @@ gptoss_status gptoss_attn_prefill(const gptoss_seq_desc* desc, const void* q, co
   // window layers, where each key tile is staged only about three times.
   const int krot = KROT_NONE;
   return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, sinks, softmax_scale, window, table,
-                      table_rows, rotary_dim, out, o_strides, workspace, workspace_bytes, krot, stream);
+                      table_rows, rotary_dim, out, o_strides, nullptr, workspace, workspace_bytes, krot, stream);
+}
+
+gptoss_status gptoss_attn_prefill_lse(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
+                                      const void* k, const int64_t k_strides[3], const void* v,
+                                      const int64_t v_strides[3], const float* sinks, float softmax_scale,
+                                      int32_t window, const void* table, int32_t table_rows,
+                                      int32_t rotary_dim, void* out, const int64_t o_strides[3], float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!lse) return fail(GPTOSS_ERR_NULL, "lse is required");
+  if (!aligned16(lse)) return fail(GPTOSS_ERR_UNSUPPORTED, "lse must be 16-byte aligned");
+  return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, sinks, softmax_scale, window, table,
+                      table_rows, rotary_dim, out, o_strides, lse, workspace, workspace_bytes, KROT_NONE, stream);
 }
 
 gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
@@ -334,7 +347,129 @@ gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc, const void* q,
     default: return fail(GPTOSS_ERR_SHAPE, "k_rotation %d is not a gptoss_k_rotation value", k_rotation);
   }
   return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, sinks, softmax_scale, window, table,
-                      table_rows, rotary_dim, out, o_strides, workspace, workspace_bytes, krot, stream);
+                      table_rows, rotary_dim, out, o_strides, nullptr, workspace, workspace_bytes, krot, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the prefill attention.
+// ---------------------------------------------------------------------------
+static int32_t thd_items(const gptoss_seq_desc* d, int bq) { return (d->seqlen + bq - 1) / bq + d->batch; }
+
+size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc) {
+  if (check_desc(desc) != GPTOSS_OK) return 0;
+  const size_t T = (size_t)desc_tokens(desc);
+  const size_t hq = (size_t)desc->num_q_heads, hkv = (size_t)desc->num_kv_heads;
+  size_t bytes = 0;
+  if (desc->layout == GPTOSS_THD)
+    bytes += round_up((size_t)thd_items(desc, kPrefillBQ) * sizeof(int2)) + kAlign +
+             round_up((size_t)thd_items(desc, kBackwardNK) * sizeof(int2)) + kAlign;
+  bytes += round_up(T * hq * kHeadDim * sizeof(uint16_t));    // rotated q
+  bytes += round_up(T * hkv * kHeadDim * sizeof(uint16_t));   // rotated k
+  bytes += round_up(T * hq * sizeof(float));                  // D = <dO, o>
+  return bytes;
+}
+
+gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
+                                           const void* k, const int64_t k_strides[3], const void* v,
+                                           const int64_t v_strides[3], const float* sinks, float softmax_scale,
+                                           int32_t window, const void* table, int32_t table_rows,
+                                           int32_t rotary_dim, const void* out, const int64_t o_strides[3],
+                                           const void* dout, const int64_t do_strides[3], const float* lse,
+                                           void* dq, void* dk, void* dv, float* dsinks, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  gptoss_status st = check_desc(desc);
+  if (st != GPTOSS_OK) return st;
+  if (!dsinks) return fail(GPTOSS_ERR_NULL, "dsinks is required");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (desc_tokens(desc) == 0 || desc->batch == 0)
+    return hip_status(launch_fill_f32(dsinks, desc->num_q_heads, 0.0f, s), "dsinks clear");
+  if (!q || !k || !v || !out || !dout || !lse || !sinks || !dq || !dk || !dv || !q_strides || !k_strides ||
+      !v_strides || !o_strides || !do_strides)
+    return fail(GPTOSS_ERR_NULL, "q, k, v, sinks, out, dout, lse, dq, dk, dv and all strides are required");
+  if (!strides_ok(q_strides, 3) || !strides_ok(k_strides, 3) || !strides_ok(v_strides, 3) ||
+      !strides_ok(o_strides, 3) || !strides_ok(do_strides, 3) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
+  if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (k_strides[1] * 2 * 64 > (int64_t)INT32_MAX || v_strides[1] * 2 * 64 > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "token strides of k and v must be below 2^24 elements");
+  st = check_table(table, table_rows, rotary_dim, desc_max_len(desc));
+  if (st != GPTOSS_OK) return st;
+  const size_t need = gptoss_attn_prefill_backward_workspace_size(desc);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return fail(GPTOSS_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  const bool thd = desc->layout == GPTOSS_THD;
+  const int64_t T = desc_tokens(desc);
+  const int32_t hq = desc->num_q_heads, hkv = desc->num_kv_heads;
+  char* ws = static_cast<char*>(workspace);
+
+  BackwardParams p;
+  memset(&p, 0, sizeof p);
+  if (thd) {
+    const int32_t nq = thd_items(desc, kPrefillBQ), nk = thd_items(desc, kBackwardNK);
+    int2* wq = reinterpret_cast<int2*>(ws);
+    ws += round_up((size_t)nq * sizeof(int2));
+    int32_t* cq = reinterpret_cast<int32_t*>(ws);
+    ws += kAlign;
+    int2* wk = reinterpret_cast<int2*>(ws);
+    ws += round_up((size_t)nk * sizeof(int2));
+    int32_t* ck = reinterpret_cast<int32_t*>(ws);
+    ws += kAlign;
+    st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, kPrefillBQ, nq, wq, cq, s), "THD schedule");
+    if (st != GPTOSS_OK) return st;
+    st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, kBackwardNK, nk, wk, ck, s), "THD schedule");
+    if (st != GPTOSS_OK) return st;
+    p.work_q = wq; p.count_q = cq; p.q_blocks = nq;
+    p.work_k = wk; p.count_k = ck; p.k_tiles = nk;
+  } else {
+    p.q_blocks = (desc->seqlen + kPrefillBQ - 1) / kPrefillBQ;
+    p.k_tiles = (desc->seqlen + kBackwardNK - 1) / kBackwardNK;
+  }
+  uint16_t* qrot = reinterpret_cast<uint16_t*>(ws);
+  ws += round_up((size_t)T * hq * kHeadDim * sizeof(uint16_t));
+  uint16_t* krot = reinterpret_cast<uint16_t*>(ws);
+  ws += round_up((size_t)T * hkv * kHeadDim * sizeof(uint16_t));
+  p.dd = reinterpret_cast<float*>(ws);
+
+  if (table) {
+    // rotate q and k once into the workspace (contiguous), exactly as the forward does
+    st = gptoss_rope_qk(desc, q, q_strides, k, k_strides, qrot, krot, table, table_rows, rotary_dim, stream);
+    if (st != GPTOSS_OK) return st;
+    p.q = qrot;
+    p.q_sh = kHeadDim; p.q_st = (int64_t)hq * kHeadDim; p.q_sb = thd ? 0 : (int64_t)desc->seqlen * p.q_st;
+    p.k = krot;
+    p.k_sh = kHeadDim; p.k_st = (int64_t)hkv * kHeadDim; p.k_sb = thd ? 0 : (int64_t)desc->seqlen * p.k_st;
+  } else {
+    p.q = static_cast<const uint16_t*>(q);
+    p.q_sb = thd ? 0 : q_strides[0]; p.q_st = q_strides[1]; p.q_sh = q_strides[2];
+    p.k = static_cast<const uint16_t*>(k);
+    p.k_sb = thd ? 0 : k_strides[0]; p.k_st = k_strides[1]; p.k_sh = k_strides[2];
+  }
+  p.v = static_cast<const uint16_t*>(v);
+  p.v_sb = thd ? 0 : v_strides[0]; p.v_st = v_strides[1]; p.v_sh = v_strides[2];
+  p.o = static_cast<const uint16_t*>(out);
+  p.o_sb = thd ? 0 : o_strides[0]; p.o_st = o_strides[1]; p.o_sh = o_strides[2];
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.do_sb = thd ? 0 : do_strides[0]; p.do_st = do_strides[1]; p.do_sh = do_strides[2];
+  p.lse = lse;
+  p.sinks = sinks;
+  p.dsinks = dsinks;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.table = static_cast<const uint16_t*>(table);
+  p.table_rows = table_rows;
+  p.batch = desc->batch;
+  p.seqlen = desc->seqlen;
+  p.num_kv_heads = hkv;
+  p.window = window;
+  p.scale = softmax_scale;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
+  return hip_status(launch_backward(p, thd, s), "backward kernels");
 }
 
 // Keys per split when the caller fixes the number of splits: a multiple of 128.

@@ -14,6 +14,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -97,7 +98,8 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
       float o2 = p2 + t2;                      // RN(x2*C + x1*S)
       r1[2 * w + h] = o1;
       r2[2 * w + h] = o2;
-      fix |= maybe_inexact_tie(o1, p1, t1) | maybe_inexact_tie(o2, p2, t2);
+      fix |= maybe_inexact_tie(o1, p1, t1);
+      fix |= maybe_inexact_tie(o2, p2, t2);
     }
   }
   if (fix) {  // rare: redo every element with the exact fix-up (a no-op where not needed)

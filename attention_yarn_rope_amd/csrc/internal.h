@@ -51,6 +51,7 @@ struct PrefillParams {
   const int32_t* cu_seqlens;     // THD
   const int2* work;              // THD work list (seq, q block), longest first
   const int32_t* work_count;     // THD: number of valid entries in `work`
+  float* lse;                    // optional fp32 [tokens, num_q_heads] log-sum-exp per row (NULL: none)
 };
 enum KRotation { KROT_NONE = 0, KROT_FUSED = 1 };
 hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_t stream);
@@ -58,6 +59,37 @@ hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_
 hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t bq, int32_t max_items,
                                int2* work, int32_t* work_count, hipStream_t stream);
 constexpr int kPrefillBQ = 32;   // query positions per work item
+
+// ---- prefill backward ----
+struct BackwardParams {
+  const uint16_t* q; int64_t q_sb, q_st, q_sh;     // rotated q (bf16)
+  const uint16_t* k; int64_t k_sb, k_st, k_sh;     // rotated k
+  const uint16_t* v; int64_t v_sb, v_st, v_sh;
+  const uint16_t* o; int64_t o_sb, o_st, o_sh;     // forward output
+  const uint16_t* dout; int64_t do_sb, do_st, do_sh;
+  const float* lse;              // [tokens, Hq] natural log, from the forward
+  float* dd;                     // workspace [tokens, Hq]: D = <dO, o>
+  const float* sinks;
+  float* dsinks;                 // [Hq]
+  uint16_t* dq; uint16_t* dk; uint16_t* dv;   // contiguous [tokens, H, 64]
+  const uint16_t* table;         // NULL: q and k were given already rotated (no rotation back)
+  int32_t table_rows;
+  int32_t batch;                 // BSHD batch, or number of THD sequences
+  int32_t seqlen;                // BSHD S, or THD total tokens
+  int32_t num_kv_heads;
+  int32_t window;
+  float scale;                   // softmax_scale
+  float scale_log2;              // softmax_scale * log2(e)
+  const int32_t* cu_seqlens;     // THD
+  int32_t q_blocks;              // BSHD: ceil(S / 32); THD: max entries of work_q
+  int32_t k_tiles;               // BSHD: ceil(S / 64); THD: max entries of work_k
+  const int2* work_q; const int32_t* count_q;   // THD: (sequence, query block), most keys first
+  const int2* work_k; const int32_t* count_k;   // THD: (sequence, key tile counted from the end), most queries first
+};
+hipError_t launch_backward(const BackwardParams& p, bool thd, hipStream_t stream);
+// x[0 .. n) = value (a kernel, not a memset: safe inside captured graphs)
+hipError_t launch_fill_f32(float* x, int32_t n, float value, hipStream_t stream);
+constexpr int kBackwardNK = 64;  // keys per tile of the backward kernels
 
 // ---- decode ----
 struct DecodeParams {

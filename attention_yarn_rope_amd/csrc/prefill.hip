@@ -94,6 +94,7 @@ void prefill_kernel(PrefillParams p) {
   const int g = blockIdx.x - item * Hkv;
   int j, L;
   int64_t bb_off_q, bb_off_k, bb_off_v, bb_off_o;  // batch offsets
+  int64_t row0;                                    // token-major row of the batch's first token (lse)
   int ts;                                          // first token of the sequence
   if (THD) {
     if (item >= __ldg(p.work_count)) return;
@@ -104,6 +105,7 @@ void prefill_kernel(PrefillParams p) {
     const int te = min(max(__ldg(p.cu_seqlens + n + 1), ts), p.seqlen);
     L = te - ts;
     bb_off_q = bb_off_k = bb_off_v = bb_off_o = 0;
+    row0 = 0;
   } else {
     const int r = item / p.batch;
     const int b = item - r * p.batch;
@@ -111,6 +113,7 @@ void prefill_kernel(PrefillParams p) {
     ts = 0;
     L = p.seqlen;
     bb_off_q = b * p.q_sb; bb_off_k = b * p.k_sb; bb_off_v = b * p.v_sb; bb_off_o = b * p.o_sb;
+    row0 = (int64_t)b * p.seqlen;
   }
   const int q0 = j * BQ;
   if (j < 0 || q0 >= L) return;
@@ -360,6 +363,11 @@ void prefill_kernel(PrefillParams p) {
     if (pos > qlast) continue;
     const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
     const int head = g * kGroup + wave * (CB / 2) + (cb >> 1);
+    if (p.lse && grp == 0) {
+      // natural log of exp(sigma) + sum exp(s): the row sum is kept relative to
+      // exp2(ref) in log2 units; -inf for a row with nothing visible and no sink
+      p.lse[(row0 + ts + pos) * (Hkv * kGroup) + head] = (l > 0.0f) ? (ref[cb] + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+    }
     bf16_t* op = p.o + bb_off_o + (int64_t)(ts + pos) * p.o_st + (int64_t)head * p.o_sh + 4 * grp;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {

@@ -108,6 +108,13 @@ def decode(num_seqs, lo, hi, seed, max_len=None, hq=HQ, hkv=HKV, d=HEAD_DIM, len
                   lengths=lengths)
 
 
+def grad_out(shape, seed):
+    """Gradient of the loss with respect to the attention output for the
+    backward pass: torch.randn(shape) rounded to bfloat16, its own generator."""
+    g = torch.Generator().manual_seed(seed)
+    return _randn_bf16(tuple(shape), g)
+
+
 # The five workloads of this attention path: a tiny prefill, a dense 4K BSHD
 # prefill, packed THD sequences, a 128K-token prefill and a 64-sequence decode.
 def tiny(seed=0):

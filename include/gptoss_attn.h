@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define GPTOSS_ABI_VERSION 1
+#define GPTOSS_ABI_VERSION 2
 
 typedef enum {
   GPTOSS_OK = 0,
@@ -179,6 +179,67 @@ gptoss_status gptoss_attn_prefill(const gptoss_seq_desc* desc,
                                   const void* table, int32_t table_rows, int32_t rotary_dim,
                                   void* out, const int64_t o_strides[3],
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptoss_attn_prefill that also writes each row's log-sum-exp, the quantity
+ * the backward pass needs (its softmax normaliser, including the sink term):
+ *   lse: device fp32 [tokens, num_q_heads] (tokens = batch * seqlen in (b, s)
+ *        order for BSHD, the packed tokens for THD), contiguous, 16-byte
+ *        aligned; lse = log(exp(sigma_h) + sum over visible j of exp(s_ij)) in
+ *        natural-log units, -INFINITY for a row with no term.
+ * Every other argument, the output and the errors are those of
+ * gptoss_attn_prefill; lse NULL returns GPTOSS_ERR_NULL. THD tokens after the
+ * last sequence are not written.
+ */
+gptoss_status gptoss_attn_prefill_lse(const gptoss_seq_desc* desc,
+                                      const void* q, const int64_t q_strides[3],
+                                      const void* k, const int64_t k_strides[3],
+                                      const void* v, const int64_t v_strides[3],
+                                      const float* sinks, float softmax_scale, int32_t window,
+                                      const void* table, int32_t table_rows, int32_t rotary_dim,
+                                      void* out, const int64_t o_strides[3], float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of gptoss_attn_prefill: the gradients of its output with
+ * respect to q, k, v and the sinks. The pages define the forward (layers page,
+ * GptOssAttention; Transformers v4.55.0 release notes, "Architecture") and
+ * describe a training framework; the gradients are the derivatives of that
+ * forward. With p_ij = exp(s_ij - lse_i), D_i = <dO_i, o_i>:
+ *   dv_j = sum_i p_ij dO_i,  dS_ij = p_ij (<dO_i, v_j> - D_i),
+ *   dq~_i = tau sum_j dS_ij k~_j,  dk~_j = tau sum_i dS_ij q~_i,
+ *   dsigma_h = - sum_i exp(sigma_h - lse_i) D_i,
+ * summed over the 8 query heads of a KV head for dk and dv. With a table, q
+ * and k are the UN-rotated inputs of the forward (rotated again here exactly
+ * as the forward rotates them) and dq = R^T dq~, dk = R^T dk~ (the rotation's
+ * transpose with the same table; the bf16 cast of the rotated values passes
+ * the gradient through).
+ *   q, k, v, sinks, softmax_scale, window, table, table_rows, rotary_dim: as
+ *            given to the forward call.
+ *   out:     the forward's bf16 output, o_strides like q_strides.
+ *   dout:    bf16 gradient of the loss with respect to out, do_strides.
+ *   lse:     the forward's log-sum-exp (gptoss_attn_prefill_lse).
+ *   dq, dk, dv: device bf16 outputs, contiguous in the layout of q, k, v
+ *            ([B, S, H, 64] or [T, H, 64]), each element written once,
+ *            rounded once from fp32 accumulation. THD tokens after the last
+ *            sequence are not written.
+ *   dsinks:  device fp32 [num_q_heads], overwritten (summed over all rows in a
+ *            fixed order: repeated calls give identical bits).
+ *   workspace: >= gptoss_attn_prefill_backward_workspace_size() bytes, 256-byte
+ *            aligned: rotated q and k, D, and the THD work lists.
+ * Errors as for gptoss_attn_prefill; every pointer except table is required.
+ */
+size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc);
+gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc,
+                                           const void* q, const int64_t q_strides[3],
+                                           const void* k, const int64_t k_strides[3],
+                                           const void* v, const int64_t v_strides[3],
+                                           const float* sinks, float softmax_scale, int32_t window,
+                                           const void* table, int32_t table_rows, int32_t rotary_dim,
+                                           const void* out, const int64_t o_strides[3],
+                                           const void* dout, const int64_t do_strides[3],
+                                           const float* lse, void* dq, void* dk, void* dv, float* dsinks,
+                                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gptoss_attn_prefill with an explicit choice of where k is rotated when a

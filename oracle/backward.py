@@ -34,6 +34,20 @@ dq = R^T dq~ and dk = R^T dk~, with R^T the rotation by the opposite angle:
 Everything is fp64 and unrounded. Pinned by tests/test_oracle_backward.py
 (finite differences of the forward, torch autograd of an independently written
 forward, closed forms).
+
+With with_noise, the functions also return the scale of the rounding noise a
+bf16/fp32 implementation adds, for the GPU tests' tolerance: each bf16 rounding
+(8 significant bits, to nearest) has a relative error of at most 2^-8, and
+independent errors add in quadrature. The kernels round dS (for dq, dk) and p (for dv) to bf16 as matrix
+operands, and form D from the bf16 forward output o. So, per element,
+  n_dq~_id^2 = tau^2 [ sum_j dS_ij^2 k~_jd^2 + E_i (sum_j p_ij k~_jd)^2 ]
+  n_dk~_jd^2 = tau^2 sum_i [ dS_ij^2 q~_id^2 + p_ij^2 E_i q~_id^2 ]
+  n_dv_jd^2  = sum_i p_ij^2 dO_id^2
+with E_i = sum_d (dO_id o_id)^2 (the o rounding inside D), rotated back like
+the gradients (squares combined with cos^2 and sin^2); and for the sink,
+  n_dsigma_h^2 = sum_i exp(sigma_h - lse_i)^2 E_i,  m_dsigma_h = sum_i |exp(sigma_h - lse_i) D_i|.
+These are magnitudes, not gradients; the error bound built from them is
+stated where it is used.
 """
 
 import numpy as np
@@ -53,10 +67,11 @@ def rotate_transpose(dy, cos, sin):
     return np.concatenate([d1 * cos + d2 * sin, d2 * cos - d1 * sin, dy[..., rd:]], axis=-1)
 
 
-def sink_attention_backward(q, k, v, sinks, scale, q_pos, k_pos, window, dout):
+def sink_attention_backward(q, k, v, sinks, scale, q_pos, k_pos, window, dout, with_noise=False):
     """One sequence, q [Tq,Hq,D] and k/v [Tk,Hkv,D] already rotated, dout [Tq,Hq,D].
 
-    Returns (o, lse, dq~, dk~, dv, dsinks): fp64, lse [Tq,Hq] natural log.
+    Returns (o, lse, dq~, dk~, dv, dsinks): fp64, lse [Tq,Hq] natural log; with
+    with_noise a seventh item, the dict of squared noise scales (module docstring).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -73,6 +88,8 @@ def sink_attention_backward(q, k, v, sinks, scale, q_pos, k_pos, window, dout):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dsinks = np.zeros(Hq)
+    nz = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+          "dsinks": np.zeros(Hq), "m_dsinks": np.zeros(Hq)}
     for h in range(Hq):
         g = h // G
         Q, K, V, dO = q[:, h], k[:, g], v[:, g], dout[:, h]
@@ -94,11 +111,40 @@ def sink_attention_backward(q, k, v, sinks, scale, q_pos, k_pos, window, dout):
         dsinks[h] = -(psink * Dr).sum()
         o[:, h] = oh
         lse[:, h] = l
+        if with_noise:
+            E = ((dO * oh) ** 2).sum(axis=1)
+            nz["dq"][:, h] = scale ** 2 * ((dS ** 2) @ (K ** 2) + E[:, None] * (p @ K) ** 2)
+            nz["dk"][:, g] += scale ** 2 * ((dS ** 2).T @ (Q ** 2) + (p ** 2).T @ (E[:, None] * Q ** 2))
+            nz["dv"][:, g] += (p ** 2).T @ (dO ** 2)
+            nz["dsinks"][h] = (psink ** 2 * E).sum()
+            nz["m_dsinks"][h] = np.abs(psink * Dr).sum()
+    if with_noise:
+        return o, lse, dq, dk, dv, dsinks, nz
     return o, lse, dq, dk, dv, dsinks
 
 
+def _rotate_noise(n2, cos, sin):
+    """Squared noise scales through R^T: the squares combine with cos^2 and sin^2."""
+    half = cos.shape[-1]
+    a, b = n2[..., :half], n2[..., half:2 * half]
+    c2, s2 = cos ** 2, sin ** 2
+    return np.concatenate([c2 * a + s2 * b, c2 * b + s2 * a, n2[..., 2 * half:]], axis=-1)
+
+
+def _finish_noise(nz, rot):
+    """Square roots of the accumulated squares; dq and dk through R^T first when rotated."""
+    out = {}
+    for name in ("dq", "dk"):
+        x = nz[name]
+        out[name] = np.sqrt(_rotate_noise(x, *rot) if rot is not None else x)
+    out["dv"] = np.sqrt(nz["dv"])
+    out["dsinks"] = np.sqrt(nz["dsinks"])
+    out["m_dsinks"] = nz["m_dsinks"]
+    return out
+
+
 def prefill_bshd_backward(q, k, v, sinks, scale, window, dout, cfg: RopeConfig = RopeConfig(),
-                          rotate_qk=True, round_rotation=True):
+                          rotate_qk=True, round_rotation=True, with_noise=False):
     """BSHD: q [B,S,Hq,D], k/v [B,S,Hkv,D], dout [B,S,Hq,D] (fp64 holding bf16 values).
 
     With rotate_qk, q and k are rotated as in the forward (rounded to bf16 unless
@@ -112,23 +158,37 @@ def prefill_bshd_backward(q, k, v, sinks, scale, window, dout, cfg: RopeConfig =
         qr, kr = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
     pos = np.arange(S)
     out = {n: [] for n in ("o", "lse", "dq", "dk", "dv")}
+    noise = {n: [] for n in ("dq", "dk", "dv")}
     dsinks = np.zeros(q.shape[2])
+    nsink = np.zeros(q.shape[2])
+    msink = np.zeros(q.shape[2])
     for b in range(B):
-        o, lse, dq, dk, dv, ds = sink_attention_backward(qr[b], kr[b], v[b], sinks, scale, pos, pos, window, dout[b])
-        for n, x in zip(("o", "lse", "dq", "dk", "dv"), (o, lse, dq, dk, dv)):
+        r = sink_attention_backward(qr[b], kr[b], v[b], sinks, scale, pos, pos, window, dout[b], with_noise)
+        for n, x in zip(("o", "lse", "dq", "dk", "dv"), r[:5]):
             out[n].append(x)
-        dsinks += ds
+        dsinks += r[5]
+        if with_noise:
+            for n in ("dq", "dk", "dv"):
+                noise[n].append(r[6][n])
+            nsink += r[6]["dsinks"]
+            msink += r[6]["m_dsinks"]
     res = {n: np.stack(x) for n, x in out.items()}
+    rot = None
     if rotate_qk:
         cos, sin = cos_sin_table(cfg, pos)
-        res["dq"] = rotate_transpose(res["dq"], cos[None, :, None, :], sin[None, :, None, :])
-        res["dk"] = rotate_transpose(res["dk"], cos[None, :, None, :], sin[None, :, None, :])
+        rot = (cos[None, :, None, :], sin[None, :, None, :])
+        res["dq"] = rotate_transpose(res["dq"], *rot)
+        res["dk"] = rotate_transpose(res["dk"], *rot)
     res["dsinks"] = dsinks
+    if with_noise:
+        nz = {n: np.stack(x) for n, x in noise.items()}
+        nz["dsinks"], nz["m_dsinks"] = nsink, msink
+        res["noise"] = _finish_noise(nz, rot)
     return res
 
 
 def prefill_thd_backward(q, k, v, cu_seqlens, sinks, scale, window, dout, cfg: RopeConfig = RopeConfig(),
-                         rotate_qk=True, round_rotation=True):
+                         rotate_qk=True, round_rotation=True, with_noise=False):
     """Packed THD: q [T,Hq,D], k/v [T,Hkv,D], dout [T,Hq,D], cu_seqlens [N+1]; positions restart per sequence."""
     T = q.shape[0]
     if rotate_qk:
@@ -139,18 +199,28 @@ def prefill_thd_backward(q, k, v, cu_seqlens, sinks, scale, window, dout, cfg: R
     res = {"o": np.zeros(q.shape[:2] + (v.shape[-1],)), "lse": np.full(q.shape[:2], -np.inf),
            "dq": np.zeros(q.shape), "dk": np.zeros(k.shape), "dv": np.zeros(v.shape),
            "dsinks": np.zeros(q.shape[1])}
+    nz = {"dq": np.zeros(q.shape), "dk": np.zeros(k.shape), "dv": np.zeros(v.shape),
+          "dsinks": np.zeros(q.shape[1]), "m_dsinks": np.zeros(q.shape[1])}
     for n in range(len(cu) - 1):
         a, b = int(cu[n]), int(cu[n + 1])
         if b <= a:
             continue
         pos = np.arange(b - a)
-        o, lse, dq, dk, dv, ds = sink_attention_backward(qr[a:b], kr[a:b], v[a:b], sinks, scale, pos, pos, window,
-                                                         dout[a:b])
-        res["o"][a:b], res["lse"][a:b], res["dq"][a:b], res["dk"][a:b], res["dv"][a:b] = o, lse, dq, dk, dv
-        res["dsinks"] += ds
+        r = sink_attention_backward(qr[a:b], kr[a:b], v[a:b], sinks, scale, pos, pos, window, dout[a:b], with_noise)
+        res["o"][a:b], res["lse"][a:b], res["dq"][a:b], res["dk"][a:b], res["dv"][a:b] = r[:5]
+        res["dsinks"] += r[5]
+        if with_noise:
+            for name in ("dq", "dk", "dv"):
+                nz[name][a:b] = r[6][name]
+            nz["dsinks"] += r[6]["dsinks"]
+            nz["m_dsinks"] += r[6]["m_dsinks"]
+    rot = None
     if rotate_qk:
         pos = thd_positions(cu, T)
         cos, sin = cos_sin_table(cfg, pos)
-        res["dq"] = rotate_transpose(res["dq"], cos[:, None, :], sin[:, None, :])
-        res["dk"] = rotate_transpose(res["dk"], cos[:, None, :], sin[:, None, :])
+        rot = (cos[:, None, :], sin[:, None, :])
+        res["dq"] = rotate_transpose(res["dq"], *rot)
+        res["dk"] = rotate_transpose(res["dk"], *rot)
+    if with_noise:
+        res["noise"] = _finish_noise(nz, rot)
     return res

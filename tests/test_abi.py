@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.gptoss_abi_version() == 1
+    assert lib.gptoss_abi_version() == 2
     for code in range(6):
         assert lib.gptoss_status_string(code)
     assert lib.gptoss_status_string(99) == b"unknown status"

@@ -1,0 +1,168 @@
+"""GPU parity of the prefill backward (dq, dk, dv, dsinks) and the forward's
+log-sum-exp against the fp64 oracle (oracle.backward), through the C ABI.
+
+Sizes span several 64-key tiles and 32-query blocks with ragged tails, full
+causal and window layers, BSHD and packed THD, one and two KV heads. The
+gradient tolerance is stated in the design doc and written in grad_close below.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_yarn_rope_amd as gx
+import oracle
+from attention_yarn_rope_amd import workloads as wl
+from helpers import np64, say
+
+pytestmark = pytest.mark.gpu
+CFG = oracle.RopeConfig()
+TAU = 0.125
+
+
+@pytest.fixture(scope="module")
+def table():
+    return gx.rope_table(16384)
+
+
+U = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits, round to nearest)
+
+
+def grad_close(got, ref, noise, what, mag=None):
+    """Elementwise |gpu - oracle| <= 4 U n + 2 U |oracle| (or 2 U mag when given).
+
+    n is the oracle's root-sum-square scale of the products whose bf16 rounding
+    the kernels make (dS and p as matrix operands, the bf16 output o inside D).
+    Each rounding errs by at most U relative, with a standard deviation of at
+    most U / sqrt(3); independent errors add in quadrature, so 4 U n is about
+    seven standard deviations. The relative term covers the bf16 rounding of
+    the result itself (U) and the forward's log-sum-exp error (at most U on p).
+    """
+    g = np64(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    err = np.abs(g - r)
+    bound = 4 * U * noise + 2 * U * (np.abs(r) if mag is None else mag) + 1e-6
+    ratio = float((err / bound).max()) if err.size else 0.0
+    rel_l2 = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+    say(f"  {what}: max_abs={float(err.max()) if err.size else 0:.3e} rel_l2={rel_l2:.3e} worst_ratio={ratio:.3f}")
+    if ratio > 1.0:
+        w = np.unravel_index(np.argmax(err / bound), err.shape)
+        say(f"    worst at {tuple(int(i) for i in w)}: gpu={g[w]:.5f} ref={r[w]:.5f} noise={noise[w]:.3e}; "
+            f"{int((err > bound).sum())} of {err.size} elements out of tolerance")
+    return ratio
+
+
+def _assert_all(ratios, what):
+    assert max(ratios) <= 1.0, f"{what}: tolerance exceeded (worst ratios {[round(x, 3) for x in ratios]})"
+
+
+def _bshd_case(B, S, window, table, seed, hq=64, hkv=8):
+    inp = wl.prefill_bshd(B, S, seed=seed, hq=hq, hkv=hkv)
+    dout = wl.grad_out((B, S, hq, 64), seed + 1000)
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    o, lse = gx.attn_prefill_lse(q, k, v, s, window=window, table=table)
+    dq, dk, dv, ds = gx.attn_prefill_backward(q, k, v, s, o, dout.cuda(), lse, window=window, table=table)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_bshd_backward(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.sinks), TAU, window,
+                                       np64(dout), CFG, with_noise=True)
+    return (o, lse, dq, dk, dv, ds), ref
+
+
+def _check(got, ref, what):
+    o, lse, dq, dk, dv, ds = got
+    lse_ref = ref["lse"].reshape(-1, ref["lse"].shape[-1])
+    # the forward sums bf16-rounded p: l is off by at most U relative, lse by U (plus fp32 log)
+    err = np.abs(np64(lse) - lse_ref)
+    say(f"  {what} lse: max_abs={float(err.max()):.3e}")
+    assert float(err.max()) <= U + 1e-4, f"{what}: lse error {float(err.max())}"
+    n = ref["noise"]
+    _assert_all([grad_close(dq, ref["dq"], n["dq"], f"{what} dq"), grad_close(dk, ref["dk"], n["dk"], f"{what} dk"),
+                 grad_close(dv, ref["dv"], n["dv"], f"{what} dv"),
+                 grad_close(ds, ref["dsinks"], n["dsinks"], f"{what} dsinks", mag=n["m_dsinks"])], what)
+
+
+def test_lse_forward_output_unchanged(table):
+    inp = wl.prefill_bshd(2, 300, seed=51)
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    say("[gpu] attn_prefill_lse output == attn_prefill output")
+    for w in (0, 128):
+        o1 = gx.attn_prefill(q, k, v, s, window=w, table=table)
+        o2, _ = gx.attn_prefill_lse(q, k, v, s, window=w, table=table)
+        assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("B,S", [(1, 256), (2, 300), (1, 129)])
+@pytest.mark.parametrize("window", [0, 128])
+def test_backward_bshd(table, B, S, window):
+    say(f"[gpu] backward bshd B={B} S={S} W={window}")
+    got, ref = _bshd_case(B, S, window, table, seed=60 + S + window)
+    _check(got, ref, f"B={B} S={S} W={window}")
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_backward_ragged_long(table, window):
+    say(f"[gpu] backward bshd B=2 S=700 W={window}")
+    got, ref = _bshd_case(2, 700, window, table, seed=90 + window)
+    _check(got, ref, f"B=2 S=700 W={window}")
+
+
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_backward_other_group_counts(table, hkv):
+    say(f"[gpu] backward Hkv={hkv}")
+    for w in (0, 64):
+        got, ref = _bshd_case(1, 300, w, table, seed=110 + hkv + w, hq=8 * hkv, hkv=hkv)
+        _check(got, ref, f"Hkv={hkv} W={w}")
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_backward_thd(table, window):
+    lengths = [37, 1, 0, 300, 128, 65, 200]
+    inp = wl.prefill_thd(0, 0, 0, seed=120 + window, lengths=lengths)
+    T = sum(lengths)
+    dout = wl.grad_out((T, 64, 64), 1120 + window)
+    say(f"[gpu] backward thd W={window}")
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    cu = inp.cu_seqlens.cuda()
+    o, lse = gx.attn_prefill_lse(q, k, v, s, window=window, table=table, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    grads = gx.attn_prefill_backward(q, k, v, s, o, dout.cuda(), lse, window=window, table=table, cu_seqlens=cu,
+                                     max_seqlen=inp.max_seqlen)
+    ref = oracle.prefill_thd_backward(np64(inp.q), np64(inp.k), np64(inp.v), inp.cu_seqlens.numpy(),
+                                      np64(inp.sinks), TAU, window, np64(dout), CFG, with_noise=True)
+    _check((o, lse) + tuple(grads), ref, f"thd W={window}")
+
+
+def test_backward_prerotated_and_deterministic(table):
+    """table = None takes q and k as already rotated: gradients then equal the
+    rotated-space ones, i.e. R^T undone; two calls give identical bits."""
+    inp = wl.prefill_bshd(1, 200, seed=130)
+    dout = wl.grad_out((1, 200, 64, 64), 1130).cuda()
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    qr, kr = gx.rope_qk(q, k, table)
+    say("[gpu] backward pre-rotated inputs, repeatability")
+    o, lse = gx.attn_prefill_lse(qr, kr, v, s, window=0)
+    g1 = gx.attn_prefill_backward(qr, kr, v, s, o, dout, lse, window=0)
+    g2 = gx.attn_prefill_backward(qr, kr, v, s, o, dout, lse, window=0)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    ref = oracle.prefill_bshd_backward(np64(qr), np64(kr), np64(inp.v), np64(inp.sinks), TAU, 0, np64(dout),
+                                       rotate_qk=False, with_noise=True)
+    _check((o, lse) + tuple(g1), ref, "pre-rotated")
+
+
+def test_backward_special_sinks(table):
+    """sigma = -inf (no sink: dsigma = 0) and a large sigma = +30 (the sink takes almost all weight)."""
+    inp = wl.prefill_bshd(1, 150, seed=140)
+    dout = wl.grad_out((1, 150, 64, 64), 1140)
+    for val in (-np.inf, 30.0):
+        sinks = torch.full((64,), float(val))
+        say(f"[gpu] backward sinks={val}")
+        q, k, v, s = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), sinks.cuda()
+        o, lse = gx.attn_prefill_lse(q, k, v, s, window=0, table=table)
+        grads = gx.attn_prefill_backward(q, k, v, s, o, dout.cuda(), lse, window=0, table=table)
+        ref = oracle.prefill_bshd_backward(np64(inp.q), np64(inp.k), np64(inp.v), sinks.double().numpy(), TAU, 0,
+                                           np64(dout), CFG, with_noise=True)
+        _check((o, lse) + tuple(grads), ref, f"sinks={val}")
+        if val == -np.inf:
+            assert torch.all(grads[3] == 0)

@@ -8,7 +8,8 @@ Each pin comes from outside oracle.backward:
     an extra logit column with a zero value row;
   * with sinks = -inf, torch's scaled_dot_product_attention backward (library);
   * lse against torch.logsumexp over [sigma, visible scores];
-  * closed forms for a single key;
+  * closed forms for a single key (gradients and the rounding-noise scales the
+    GPU tests' tolerance uses);
   * THD equals per-sequence BSHD; the gradients of GQA sum over the group.
 """
 
@@ -186,3 +187,29 @@ def test_rotate_transpose_is_the_adjoint():
     rx = oracle.rotate(x, c, s, round_output=False)
     rty = oracle.rotate_transpose(y, c, s)
     assert np.isclose((rx * y).sum(), (x * rty).sum(), rtol=1e-12)
+
+
+def test_noise_scales_single_key_closed_form():
+    """Noise scales for one key: p = e^s / (e^sigma + e^s), o = p v, dS = p (1 - p) <dO, v>,
+    E = sum_d (dO_d o_d)^2; n_dv^2 = sum_h p_h^2 dO_h^2; n_dq~^2 = tau^2 (dS^2 k^2 + E p^2 k^2);
+    n_dsigma^2 = (1 - p)^2 E; m_dsigma = |(1 - p) p <dO, v>|."""
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 1, 8, 64))
+    k = rng.standard_normal((1, 1, 1, 64))
+    v = rng.standard_normal((1, 1, 1, 64))
+    dout = rng.standard_normal((1, 1, 8, 64))
+    sinks = rng.standard_normal(8)
+    n = oracle.prefill_bshd_backward(q, k, v, sinks, TAU, 0, dout, rotate_qk=False, with_noise=True)["noise"]
+    pv = np.zeros(8)
+    for h in range(8):
+        s = TAU * float(q[0, 0, h] @ k[0, 0, 0])
+        p = np.exp(s) / (np.exp(sinks[h]) + np.exp(s))
+        pv[h] = p
+        dvd = float(dout[0, 0, h] @ v[0, 0, 0])
+        E = float(((dout[0, 0, h] * p * v[0, 0, 0]) ** 2).sum())
+        ds = p * (1 - p) * dvd
+        kk = k[0, 0, 0]
+        assert np.allclose(n["dq"][0, 0, h], TAU * np.sqrt(ds ** 2 * kk ** 2 + E * p ** 2 * kk ** 2), rtol=1e-11)
+        assert np.isclose(n["dsinks"][h], (1 - p) * np.sqrt(E), rtol=1e-11)
+        assert np.isclose(n["m_dsinks"][h], abs((1 - p) * p * dvd), rtol=1e-11)
+    assert np.allclose(n["dv"][0, 0, 0], np.sqrt((pv[:, None] ** 2 * dout[0, 0] ** 2).sum(0)), rtol=1e-11)
