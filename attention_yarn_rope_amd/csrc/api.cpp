@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -365,7 +366,7 @@ size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc) 
              round_up((size_t)thd_items(desc, kBackwardNK) * sizeof(int2)) + kAlign;
   bytes += round_up(T * hq * kHeadDim * sizeof(uint16_t));    // rotated q
   bytes += round_up(T * hkv * kHeadDim * sizeof(uint16_t));   // rotated k
-  bytes += round_up(T * hq * sizeof(float));                  // D = <dO, o>
+  bytes += 2 * round_up(T * hq * sizeof(float));              // D = <dO, o> and lse (log2), head-major
   return bytes;
 }
 
@@ -404,6 +405,10 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   const bool thd = desc->layout == GPTOSS_THD;
   const int64_t T = desc_tokens(desc);
   const int32_t hq = desc->num_q_heads, hkv = desc->num_kv_heads;
+  // one sequence's q and dO rows (plus a query block of slack) are addressed with 32-bit byte offsets
+  const int64_t q_row = table ? (int64_t)hq * kHeadDim : q_strides[1];
+  if (((int64_t)desc_max_len(desc) + 64) * 2 * std::max(q_row, do_strides[1]) > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "a sequence's q / dout rows must span less than 2 GiB");
   char* ws = static_cast<char*>(workspace);
 
   BackwardParams p;
@@ -433,6 +438,9 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   uint16_t* krot = reinterpret_cast<uint16_t*>(ws);
   ws += round_up((size_t)T * hkv * kHeadDim * sizeof(uint16_t));
   p.dd = reinterpret_cast<float*>(ws);
+  ws += round_up((size_t)T * hq * sizeof(float));
+  p.lse2 = reinterpret_cast<float*>(ws);
+  p.tokens = T;
 
   if (table) {
     // rotate q and k once into the workspace (contiguous), exactly as the forward does

@@ -46,17 +46,17 @@ constexpr int QS = 80;           // LDS row stride of a wave's q / dO tile (dk/d
 __device__ __forceinline__ uint2 ldg8(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
 // ---------------------------------------------------------------------------
-// D = <dO, o> per (token, query head): 8 lanes per row, 8 dims each.
+// D = <dO, o> per (token, query head), and lse in log2 units, both written
+// head-major [Hq, tokens] so the kernels below read a head's consecutive rows
+// contiguously. Work group: 32 tokens of one head, 8 lanes per row.
 // ---------------------------------------------------------------------------
 template <bool THD>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BackwardParams p) {
   const int Hq = p.num_kv_heads * kGroup;
-  const int64_t tokens = THD ? (int64_t)p.seqlen : (int64_t)p.batch * p.seqlen;
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int h = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int c = threadIdx.x & 7;
-  if (row >= tokens * Hq) return;   // whole 8-lane groups leave together
-  const int64_t t = row / Hq;
-  const int h = (int)(row - t * Hq);
+  if (t >= p.tokens) return;   // whole 8-lane groups leave together
   bool valid = true;
   int64_t oo, od;
   if (THD) {
@@ -79,24 +79,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BackwardParams p) {
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
-  if (c == 0) p.dd[row] = acc;
+  if (c == 0) {
+    const float l = valid ? p.lse[t * Hq + h] : -INFINITY;
+    p.dd[(int64_t)h * p.tokens + t] = acc;
+    // a row without any term (lse = -inf) gets +inf: its probabilities exp2(x - lse2) are 0
+    p.lse2[(int64_t)h * p.tokens + t] = (l > -INFINITY) ? l * kLog2e : INFINITY;
+  }
 }
 
 // dsigma_h = - sum over the head's rows of exp(sigma_h - lse) * D, one work
 // group per head, each thread summing a fixed stride of rows, then a tree.
-__global__ __launch_bounds__(256) void bwd_sink_kernel(BackwardParams p, int32_t thd) {
+__global__ __launch_bounds__(256) void bwd_sink_kernel(BackwardParams p) {
   __shared__ float part[256];
   const int h = blockIdx.x;
-  const int Hq = p.num_kv_heads * kGroup;
-  const int64_t tokens = thd ? (int64_t)min(max(__ldg(p.cu_seqlens + p.batch), 0), p.seqlen)
-                             : (int64_t)p.batch * p.seqlen;
-  const float sig = p.sinks[h];
+  const float sig2 = p.sinks[h] * kLog2e;
+  const float* l2 = p.lse2 + (int64_t)h * p.tokens;
+  const float* dd = p.dd + (int64_t)h * p.tokens;
   float acc = 0.0f;
-  if (sig > -INFINITY) {
-    for (int64_t t = threadIdx.x; t < tokens; t += 256) {
-      const float l = p.lse[t * Hq + h];
-      if (l > -INFINITY) acc -= __builtin_amdgcn_exp2f((sig - l) * kLog2e) * p.dd[t * Hq + h];
-    }
+  if (sig2 > -INFINITY) {
+    for (int64_t t = threadIdx.x; t < p.tokens; t += 256) acc -= __builtin_amdgcn_exp2f(sig2 - l2[t]) * dd[t];
   }
   part[threadIdx.x] = acc;
   __syncthreads();
@@ -133,7 +134,7 @@ template <bool THD, bool ROT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_k[2 * NK * KSB];
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * NK * VSB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int Hkv = p.num_kv_heads, Hq = Hkv * kGroup;
   const int item = blockIdx.x / Hkv;
@@ -201,9 +202,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     qf[cb][1] = as_bf16x8(ldg16(qp + 32));
     df[cb][0] = as_bf16x8(ldg16(dp));
     df[cb][1] = as_bf16x8(ldg16(dp + 32));
-    const int64_t rr = (row0 + ts + pos) * Hq + head;
-    const float l = p.lse[rr];
-    lse2[cb] = (l > -INFINITY) ? l * kLog2e : INFINITY;   // a row without any term has no gradient
+    const int64_t rr = (int64_t)head * p.tokens + row0 + ts + pos;
+    lse2[cb] = p.lse2[rr];
     dd[cb] = p.dd[rr];
   }
 
@@ -309,18 +309,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: one work group of 4 waves per (sequence, KV head g, 64 keys); wave w
-// owns query heads 8 g + 2 w and 8 g + 2 w + 1.
+// dv (PART 0) or dk (PART 1): one work group of 4 waves per (sequence, KV head
+// g, 64 keys); wave w owns query heads 8 g + 2 w and 8 g + 2 w + 1. The two
+// gradients are separate launches so each wave holds one 64-key x 64-dim fp32
+// accumulator (64 VGPRs) and two waves fit on a SIMD; S = Q K^T is formed in
+// both (its 16 MFMAs per step are the price).
 // ---------------------------------------------------------------------------
-constexpr int kDkdvLds = 4 * 16 * 64 * 16;   // the cross-wave sum: 4 waves x 16 fragments x 64 lanes x 16 B
-static_assert(4 * 2 * BQ * QS * 2 <= kDkdvLds, "per-wave q / dO tiles fit in the reduction space");
+constexpr int kKvLds = 4 * 16 * 64 * 16;   // cross-wave sum: 4 waves x 16 fragments x 64 lanes x 16 B
+static_assert(4 * BQ * QS * 2 <= kKvLds, "per-wave transpose tiles fit in the reduction space");
 
-template <bool THD, bool ROT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[kDkdvLds];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <bool THD, bool ROT, int PART>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_kernel(BackwardParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[kKvLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int Hkv = p.num_kv_heads, Hq = Hkv * kGroup;
+  const int Hkv = p.num_kv_heads;
   const int item = blockIdx.x / Hkv;
   const int g = blockIdx.x - item * Hkv;
   int jt, L, ts;
@@ -349,165 +352,195 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int qhi = (W > 0) ? min(L - 1, tlast + W - 1) : L - 1;   // last query that sees a key of the tile
   const float sl = p.scale_log2;
 
-  // K and V of the tile as B-operand fragments: lane = key column, 8 consecutive dims
+  // K (and, for dk, V) of the tile as B-operand fragments: lane = key column, 8 consecutive dims
   bf16x8_t kf[4][2], vf[4][2];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int key = min(t0 + kb * 16 + col, tlast);
     const bf16_t* kp = p.k + bk_ + (int64_t)(ts + key) * p.k_st + (int64_t)g * p.k_sh + 8 * grp;
-    const bf16_t* vp = p.v + bv_ + (int64_t)(ts + key) * p.v_st + (int64_t)g * p.v_sh + 8 * grp;
     kf[kb][0] = as_bf16x8(ldg16(kp));
     kf[kb][1] = as_bf16x8(ldg16(kp + 32));
-    vf[kb][0] = as_bf16x8(ldg16(vp));
-    vf[kb][1] = as_bf16x8(ldg16(vp + 32));
+    if (PART == 1) {
+      const bf16_t* vp = p.v + bv_ + (int64_t)(ts + key) * p.v_st + (int64_t)g * p.v_sh + 8 * grp;
+      vf[kb][0] = as_bf16x8(ldg16(vp));
+      vf[kb][1] = as_bf16x8(ldg16(vp + 32));
+    }
   }
-  f32x4_t dkt[4][4], dvt[4][4];   // [d block][key block]: element r = dim 16*db + 4*grp + r, key col
+  f32x4_t acc[4][4];   // [d block][key block]: element r = dim 16*db + 4*grp + r, key col (dV^T or dK^T)
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) dkt[a][b] = dvt[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  bf16_t* lq = reinterpret_cast<bf16_t*>(lds_raw) + wave * (2 * BQ * QS);   // this wave's q tile [32][QS]
-  bf16_t* ldo = lq + BQ * QS;                                               // and its dO tile
+  // this wave's tile [32 queries][QS] for the transpose reads: dO (dv) or q (dk)
+  bf16_t* lt = reinterpret_cast<bf16_t*>(lds_raw) + wave * (BQ * QS);
 
-  for (int qb = t0 / BQ; qb * BQ <= qhi; ++qb) {
+  // Steps: every block of 32 queries that can see the tile, once per head of the
+  // wave (head 8 g + 2 wave + hh). In dv the global loads of the next step are in
+  // flight while a step computes.
+  const int qb_lo = t0 / BQ;
+  // Rows are read through buffer ranges that end with the sequence: rows past it
+  // read as zeros (their dO is 0, so they add nothing to dV or dK) and need no
+  // clamps; one 32-bit offset per load. The ranges of the wave's two heads are
+  // wave-uniform.
+  const int32_t qrow_b = (int32_t)p.q_st * 2, drow_b = (int32_t)p.do_st * 2;   // < 2^31 / (L + 32): host check
+  __amdgpu_buffer_rsrc_t rq[2], rd[2], rl[2], rdd[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int head = g * kGroup + 2 * wave + hh;
+    rq[hh] = make_rsrc(p.q + bq_ + (int64_t)ts * p.q_st + (int64_t)head * p.q_sh, (L - 1) * qrow_b + 2 * kHeadDim);
+    rd[hh] = make_rsrc(p.dout + bd_ + (int64_t)ts * p.do_st + (int64_t)head * p.do_sh, (L - 1) * drow_b + 2 * kHeadDim);
+    rl[hh] = make_rsrc(p.lse2 + (int64_t)head * p.tokens + row0 + ts, L * 4);
+    rdd[hh] = make_rsrc(p.dd + (int64_t)head * p.tokens + row0 + ts, L * 4);
+  }
+  struct Fetch { uint4 qa[2][2], da[2][2]; float l2[2][4], dd[2][4]; };
+  // hh is a constant at every call (the calls are unrolled), so the ranges stay scalar
+  auto fetch = [&](int qb, int hh, Fetch& f) __attribute__((always_inline)) {
+    const int q0 = qb * BQ;
+    const __amdgpu_buffer_rsrc_t bq = rq[hh], bd = rd[hh], bl = rl[hh], bdd = rdd[hh];
+#pragma unroll
+    for (int qm = 0; qm < 2; ++qm) {
+      // q~ and dO rows as A-operand fragments (lane = query row, 8 consecutive dims)
+      const uint32_t qo = (uint32_t)((q0 + qm * 16 + col) * qrow_b + 16 * grp);
+      const uint32_t dof = (uint32_t)((q0 + qm * 16 + col) * drow_b + 16 * grp);
+      f.qa[qm][0] = ldb16(bq, qo); f.qa[qm][1] = ldb16(bq, qo + 64);
+      f.da[qm][0] = ldb16(bd, dof); f.da[qm][1] = ldb16(bd, dof + 64);
+      // lse (log2 units) and D of the lane's queries q0 + 16 qm + 4 grp + e
+      const uint32_t lo = (uint32_t)((q0 + qm * 16 + 4 * grp) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f.l2[qm][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bl, lo + 4 * e, 0, 0));
+        if (PART == 1) f.dd[qm][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bdd, lo + 4 * e, 0, 0));
+      }
+    }
+  };
+  auto step = [&](int qb, const Fetch& f) __attribute__((always_inline)) {
     const int q0 = qb * BQ;
     const bool full = (q0 >= t0 + NK - 1) && (W == 0 || q0 + BQ - 1 - t0 < W);
-#pragma unroll 1
-    for (int hh = 0; hh < 2; ++hh) {
-      const int head = g * kGroup + 2 * wave + hh;
-      // q~ and dO rows as A-operand fragments (lane = query row, 8 consecutive dims)
-      uint4 qa[2][2], da[2][2];
-#pragma unroll
-      for (int qm = 0; qm < 2; ++qm) {
-        const int qr = min(q0 + qm * 16 + col, L - 1);
-        const bf16_t* qp = p.q + bq_ + (int64_t)(ts + qr) * p.q_st + (int64_t)head * p.q_sh + 8 * grp;
-        const bf16_t* dp = p.dout + bd_ + (int64_t)(ts + qr) * p.do_st + (int64_t)head * p.do_sh + 8 * grp;
-        qa[qm][0] = ldg16(qp); qa[qm][1] = ldg16(qp + 32);
-        da[qm][0] = ldg16(dp); da[qm][1] = ldg16(dp + 32);
-      }
-      // lse (log2 units) and D of the lane's queries q0 + 16 qm + 4 grp + e; rows past the
-      // sequence get lse = +inf, so their probabilities are 0
-      float lse2[2][4], dd[2][4];
-#pragma unroll
-      for (int qm = 0; qm < 2; ++qm)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qq = q0 + qm * 16 + 4 * grp + e;
-          const int64_t rr = (row0 + ts + min(qq, L - 1)) * Hq + head;
-          const float l = p.lse[rr];
-          lse2[qm][e] = (qq < L && l > -INFINITY) ? l * kLog2e : INFINITY;
-          dd[qm][e] = p.dd[rr];
-        }
-      // the previous block's transpose reads are complete before the tiles are rewritten
+    {
+      const uint4 (&qa)[2][2] = f.qa;
+      const uint4 (&da)[2][2] = f.da;
+      const float (&lse2)[2][4] = f.l2;
+      const float (&dd)[2][4] = f.dd;
+      // the previous step's transpose reads are complete before the tile is rewritten
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int qm = 0; qm < 2; ++qm)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          *reinterpret_cast<uint4*>(lq + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = qa[qm][ks];
-          *reinterpret_cast<uint4*>(ldo + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = da[qm][ks];
-        }
+        for (int ks = 0; ks < 2; ++ks)
+          *reinterpret_cast<uint4*>(lt + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = PART ? qa[qm][ks] : da[qm][ks];
 
-      // S = Q K^T and dP = dO V^T: [qm][kb] element e = query q0 + 16 qm + 4 grp + e, key t0 + 16 kb + col
-      f32x4_t s[2][4], dpm[2][4];
+      // Per 16-query half qm: S = Q K^T (and dP = dO V^T) with [kb] element e = query
+      // q0 + 16 qm + 4 grp + e, key t0 + 16 kb + col; then P (dv) or dS = P (dP - D) (dk),
+      // packed as the B operand over the 32 queries (elements 4 qm .. 4 qm + 3)
+      uint32_t bw[4][4];   // [kb][word]
 #pragma unroll
-      for (int qm = 0; qm < 2; ++qm)
+      for (int qm = 0; qm < 2; ++qm) {
+        f32x4_t s_[4], dp_[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          s[qm][kb] = mfma16(as_bf16x8(qa[qm][1]), kf[kb][1], mfma16(as_bf16x8(qa[qm][0]), kf[kb][0], z));
-          dpm[qm][kb] = mfma16(as_bf16x8(da[qm][1]), vf[kb][1], mfma16(as_bf16x8(da[qm][0]), vf[kb][0], z));
+          s_[kb] = mfma16(as_bf16x8(qa[qm][1]), kf[kb][1], mfma16(as_bf16x8(qa[qm][0]), kf[kb][0], z));
+          if (PART == 1)
+            dp_[kb] = mfma16(as_bf16x8(da[qm][1]), vf[kb][1], mfma16(as_bf16x8(da[qm][0]), vf[kb][0], z));
         }
-      if (!full) {
-#pragma unroll
-        for (int qm = 0; qm < 2; ++qm)
+        if (!full) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int qq = q0 + qm * 16 + 4 * grp + e, key = t0 + kb * 16 + col;
-              s[qm][kb][e] = ((uint32_t)(qq - key) < weff) ? s[qm][kb][e] : -INFINITY;
+              s_[kb][e] = ((uint32_t)(qq - key) < weff) ? s_[kb][e] : -INFINITY;
             }
-      }
-      // P and dS, packed as B operands over the 32 queries (e < 4: 4 grp + e of the
-      // first 16, e >= 4: of the second 16)
-      bf16x8_t pb[4], dsb[4];
+        }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        float pv[2][4], dv_[2][4];
-#pragma unroll
-        for (int qm = 0; qm < 2; ++qm)
+        for (int kb = 0; kb < 4; ++kb) {
+          float x[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pv[qm][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qm][kb][e], sl, -lse2[qm][e]));
-            dv_[qm][e] = pv[qm][e] * (dpm[qm][kb][e] - dd[qm][e]);
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[kb][e], sl, -lse2[qm][e]));
+            x[e] = (PART == 1) ? pr * (dp_[kb][e] - dd[qm][e]) : pr;
           }
-        pb[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
-                                                         pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])));
-        dsb[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(dv_[0][0], dv_[0][1]), pack_bf16x2(dv_[0][2], dv_[0][3]),
-                                                          pack_bf16x2(dv_[1][0], dv_[1][1]), pack_bf16x2(dv_[1][2], dv_[1][3])));
+          bw[kb][2 * qm] = pack_bf16x2(x[0], x[1]);
+          bw[kb][2 * qm + 1] = pack_bf16x2(x[2], x[3]);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
-      // dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T read transposed from the wave's tiles)
+      // dV^T += dO^T P (dv) or dK^T += Q^T dS (dk), the first operand read transposed from the tile
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int off = (4 * grp + (col >> 2)) * QS + 16 * db + 4 * (col & 3);
-        const uint2 dlo = lds_read_tr16(ldo + off), dhi = lds_read_tr16(ldo + off + 16 * QS);
-        const uint2 qlo = lds_read_tr16(lq + off), qhi2 = lds_read_tr16(lq + off + 16 * QS);
-        const bf16x8_t a_do = __builtin_bit_cast(bf16x8_t, make_uint4(dlo.x, dlo.y, dhi.x, dhi.y));
-        const bf16x8_t a_q = __builtin_bit_cast(bf16x8_t, make_uint4(qlo.x, qlo.y, qhi2.x, qhi2.y));
+        const uint2 lo = lds_read_tr16(lt + off), hi = lds_read_tr16(lt + off + 16 * QS);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          dvt[db][kb] = mfma16(a_do, pb[kb], dvt[db][kb]);
-          dkt[db][kb] = mfma16(a_q, dsb[kb], dkt[db][kb]);
-        }
+        for (int kb = 0; kb < 4; ++kb)
+          acc[db][kb] = mfma16(a, __builtin_bit_cast(bf16x8_t, make_uint4(bw[kb][0], bw[kb][1], bw[kb][2], bw[kb][3])),
+                               acc[db][kb]);
+      }
+    }
+  };
+  // Query blocks are walked from the last one down: the work groups of one
+  // (sequence, KV head) run together on one XCD (consecutive work groups take
+  // consecutive KV heads, dealt round-robin over the 8 XCDs) and then read the
+  // same q / dO block at about the same time, so L2 serves the repeats.
+  const int qb_hi = qhi / BQ;
+  if (PART == 0) {
+    // dv holds two fetch buffers in turn: each step computes from one while the
+    // other receives the next step's rows, with no register copies between steps
+    Fetch fa, fb;
+    fetch(qb_hi, 0, fa);
+    for (int qb = qb_hi; qb >= qb_lo; --qb) {
+      fetch(qb, 1, fb);
+      step(qb, fa);
+      fetch(max(qb - 1, qb_lo), 0, fa);   // the last block fetches itself again: no branch
+      step(qb, fb);
+    }
+  } else {
+    // dk has no registers to spare for a second buffer: each step loads its own rows
+    for (int qb = qb_hi; qb >= qb_lo; --qb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        Fetch f;
+        fetch(qb, hh, f);
+        step(qb, f);
       }
     }
   }
 
-  // sum the 4 waves' partial dK^T, dV^T through LDS; wave w finishes d blocks
-  // (w & 1, (w & 1) + 2) -- the rotation pairs dims i and i + 32 -- of key blocks
-  // 2 (w >> 1) and 2 (w >> 1) + 1
+  // sum the 4 waves' partials through LDS; wave w finishes d blocks (w & 1, (w & 1) + 2)
+  // -- the rotation pairs dims i and i + 32 -- of key blocks 2 (w >> 1) and 2 (w >> 1) + 1
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds_raw);
   const int pr = wave & 1, kh = wave >> 1;
-#pragma unroll 1
-  for (int which = 0; which < 2; ++which) {
-    __syncthreads();
+  __syncthreads();
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) red[(wave * 16 + db * 4 + kb) * 64 + lane] = which ? dvt[db][kb] : dkt[db][kb];
-    __syncthreads();
+    for (int kb = 0; kb < 4; ++kb) red[(wave * 16 + db * 4 + kb) * 64 + lane] = acc[db][kb];
+  __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kb = 2 * kh + kk;
-      const int key = t0 + kb * 16 + col;
-      f32x4_t y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < 2; ++kk) {
+    const int kb = 2 * kh + kk;
+    const int key = t0 + kb * 16 + col;
+    f32x4_t y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        y1 += red[(w * 16 + pr * 4 + kb) * 64 + lane];
-        y2 += red[(w * 16 + (pr + 2) * 4 + kb) * 64 + lane];
-      }
-      if (key > tlast) continue;
-      uint16_t* out;
-      if (which == 0) {
-        y1 *= p.scale;
-        y2 *= p.scale;
-        if (ROT) {
-          const bf16_t* tp = p.table + (int64_t)min(key, p.table_rows - 1) * kHeadDim + 16 * pr + 4 * grp;
-          rotate_back4(y1, y2, ldg8(tp), ldg8(tp + 32));
-        }
-        out = p.dk;
-      } else {
-        out = p.dv;
-      }
-      bf16_t* op = out + ((row0 + ts + key) * Hkv + g) * kHeadDim + 16 * pr + 4 * grp;
-      *reinterpret_cast<uint2*>(op) = pack4(y1);
-      *reinterpret_cast<uint2*>(op + 32) = pack4(y2);
+    for (int w = 0; w < 4; ++w) {
+      y1 += red[(w * 16 + pr * 4 + kb) * 64 + lane];
+      y2 += red[(w * 16 + (pr + 2) * 4 + kb) * 64 + lane];
     }
+    if (key > tlast) continue;
+    if (PART == 1) {
+      y1 *= p.scale;
+      y2 *= p.scale;
+      if (ROT) {
+        const bf16_t* tp = p.table + (int64_t)min(key, p.table_rows - 1) * kHeadDim + 16 * pr + 4 * grp;
+        rotate_back4(y1, y2, ldg8(tp), ldg8(tp + 32));
+      }
+    }
+    bf16_t* op = (PART == 1 ? p.dk : p.dv) + ((row0 + ts + key) * Hkv + g) * kHeadDim + 16 * pr + 4 * grp;
+    *reinterpret_cast<uint2*>(op) = pack4(y1);
+    *reinterpret_cast<uint2*>(op + 32) = pack4(y2);
   }
 }
 
@@ -520,14 +553,14 @@ template <bool THD, bool ROT>
 hipError_t launch_all(const BackwardParams& p, hipStream_t stream) {
   const int Hq = p.num_kv_heads * kGroup;
   const int64_t tokens = THD ? (int64_t)p.seqlen : (int64_t)p.batch * p.seqlen;
-  const int64_t pre_threads = tokens * Hq * 8;
-  hipLaunchKernelGGL(bwd_pre_kernel<THD>, dim3((uint32_t)((pre_threads + 255) / 256)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(bwd_sink_kernel, dim3(Hq), dim3(256), 0, stream, p, (int32_t)THD);
+  hipLaunchKernelGGL(bwd_pre_kernel<THD>, dim3((uint32_t)((tokens + 31) / 32), Hq), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(bwd_sink_kernel, dim3(Hq), dim3(256), 0, stream, p);
   const int64_t rep = THD ? 1 : p.batch;
   hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)), dim3(512), 0,
                      stream, p);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<THD, ROT>), dim3((uint32_t)(p.k_tiles * rep * p.num_kv_heads)), dim3(256), 0,
-                     stream, p);
+  const dim3 kv_grid((uint32_t)(p.k_tiles * rep * p.num_kv_heads));
+  hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT, 0>), kv_grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT, 1>), kv_grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

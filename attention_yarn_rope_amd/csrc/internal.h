@@ -68,7 +68,9 @@ struct BackwardParams {
   const uint16_t* o; int64_t o_sb, o_st, o_sh;     // forward output
   const uint16_t* dout; int64_t do_sb, do_st, do_sh;
   const float* lse;              // [tokens, Hq] natural log, from the forward
-  float* dd;                     // workspace [tokens, Hq]: D = <dO, o>
+  float* lse2;                   // workspace [Hq, tokens]: lse in log2 units, +inf for rows without a gradient
+  float* dd;                     // workspace [Hq, tokens]: D = <dO, o>
+  int64_t tokens;                // rows of the token-major tensors (BSHD batch * seqlen, THD seqlen)
   const float* sinks;
   float* dsinks;                 // [Hq]
   uint16_t* dq; uint16_t* dk; uint16_t* dv;   // contiguous [tokens, H, 64]

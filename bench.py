@@ -15,8 +15,11 @@ every call inside the timed region; the whole region is bracketed by device
 synchronisation. The CPU baseline is the fp64 oracle on a time-bounded sample
 of query rows of the same workload, on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --profile {prefill-full,prefill-window,decode-full,copy} --steps K
+The backward pass of both layers (dq, dk, dv, dsinks) is timed after the step and
+reported under "backward" (not part of `value`).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
+       python bench.py --profile {prefill-full,prefill-window,decode-full,copy,backward-full,backward-window} --steps K
        (the --profile modes run only the named call, for rocprofv3)
 """
 
@@ -139,7 +142,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--k-rotation", default="auto", choices=["auto", "fused", "separate"])
-    ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy"])
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy",
+                                                        "backward-full", "backward-window"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -194,6 +199,28 @@ def main():
         log(f"{args.profile}: {args.steps} launches")
         return
 
+    # ---------------- backward of both layers (measured beside the step) ----------------
+    def backward_calls():
+        """One forward with lse per layer, then closures that run each layer's backward."""
+        dout = wl.grad_out(q.shape, 7).to(dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty(q.shape[2], dtype=torch.float32, device=dev))
+        bws = torch.empty(max(gx.prefill_backward_workspace_size(q, k), 1), dtype=torch.uint8, device=dev)
+        calls = {}
+        for name, w in (("full", 0), ("window128", WINDOW)):
+            o, lse = gx.attn_prefill_lse(q, k, v, sinks, window=w, table=table)
+            calls[name] = (lambda o=o, lse=lse, w=w: gx.attn_prefill_backward(
+                q, k, v, sinks, o, dout, lse, window=w, table=table, workspace=bws, grads=grads))
+        return calls
+
+    if args.profile in ("backward-full", "backward-window"):
+        fn = backward_calls()["full" if args.profile == "backward-full" else "window128"]
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"{args.profile}: {args.steps} calls")
+        return
+
     lengths = [S] * q.shape[0]
     flops_full = wl.prefill_flops(lengths, 0)
     flops_win = wl.prefill_flops(lengths, WINDOW)
@@ -218,6 +245,33 @@ def main():
         log(f"[bench] prefill step {ms_step:.3f} ms (full {ms_full:.3f} ms, window {ms_win:.3f} ms, "
             f"table {ms_table:.4f} ms)")
         del timer
+
+    backward_obj = None
+    if args.profile is None and not args.no_backward:
+        calls = backward_calls()
+        timer = Timer(torch)
+        for _ in range(args.warmup):
+            for fn in calls.values():
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            for name, fn in calls.items():
+                timer.run(name, fn)
+        torch.cuda.synchronize()
+        backward_obj = {
+            "workload": "backward of the same two layers (dq, dk, dv, dsinks; dO ~ N(0,1) bf16), "
+                        "q and k rotated inside the call",
+            "flop_count": "10 * D * Hq per visible (query, key) pair: recomputed S, dP, dV, dQ, dK "
+                          "(the kernels execute 14: S and dP are formed in both the dq and the dk/dv kernel)",
+        }
+        for name, fl in (("full", flops_full), ("window128", flops_win)):
+            ms = timer.mean_ms(name)
+            bfl = fl * 5 // 2
+            backward_obj[name] = {"ms": round(ms, 4), "TFLOP/s": round(bfl / (ms * 1e-3) / 1e12, 2), "flops": bfl,
+                                  "frac_mfma_peak": round(bfl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] backward full {backward_obj['full']['ms']:.3f} ms "
+            f"({backward_obj['full']['TFLOP/s']:.0f} TFLOP/s), window {backward_obj['window128']['ms']:.3f} ms")
+        del calls, timer
 
     # ---------------- decode ----------------
     decode_obj = None
@@ -309,6 +363,7 @@ def main():
                           "flops": flops_win, "bytes": bytes_prefill},
             "table_ms": round(ms_table, 5),
         },
+        "backward": backward_obj,
         "decode": decode_obj,
         "cpu_baseline": None,
     }
