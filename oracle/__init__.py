@@ -46,7 +46,8 @@ from .attention import (
     prefill_rows,
     decode,
 )
-from .backward import rotate_transpose, sink_attention_backward, prefill_bshd_backward, prefill_thd_backward
+from .backward import (rotate_transpose, sink_attention_backward, prefill_bshd_backward, prefill_thd_backward,
+                       prefill_backward_rows)
 
 __all__ = [
     "round_bf16", "bf16_bits", "from_bf16_bits",
@@ -54,4 +55,5 @@ __all__ = [
     "rotate", "rope_qk_bshd", "rope_qk_thd", "thd_positions",
     "sink_attention", "prefill_bshd", "prefill_thd", "prefill_rows", "decode",
     "rotate_transpose", "sink_attention_backward", "prefill_bshd_backward", "prefill_thd_backward",
+    "prefill_backward_rows",
 ]

@@ -53,7 +53,7 @@ stated where it is used.
 import numpy as np
 
 from .attention import _visible
-from .rope import rope_qk_bshd, rope_qk_thd, thd_positions
+from .rope import rotate, rope_qk_bshd, rope_qk_thd, thd_positions
 from .yarn import RopeConfig, cos_sin_table
 
 
@@ -224,3 +224,47 @@ def prefill_thd_backward(q, k, v, cu_seqlens, sinks, scale, window, dout, cfg: R
     if with_noise:
         res["noise"] = _finish_noise(nz, rot)
     return res
+
+
+def prefill_backward_rows(q, k, v, sinks, scale, window, dout, q_rows, key_lo, key_hi,
+                          cfg: RopeConfig = RopeConfig()):
+    """Selected gradients of one sequence: q [S,Hq,D], k/v [S,Hkv,D] un-rotated
+    (fp64 holding bf16 values), dout [S,Hq,D]; positions 0..S-1.
+
+    Returns dq for the query rows q_rows and dk, dv for the keys key_lo..key_hi-1,
+    with their noise scales (module docstring). Each equals the matching entry of
+    prefill_bshd_backward: dq of a row depends on that row's visible keys only,
+    and every query that sees one of the keys is included for dk and dv (the
+    queries before key_lo cannot see them), so leaving the rest out changes nothing.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    S = q.shape[0]
+    out = {}
+    # dq: the rows and every key they see
+    klo = 0 if window <= 0 else max(0, int(q_rows.min()) - window + 1)
+    kr = np.arange(klo, int(q_rows.max()) + 1)
+    cq, sq = cos_sin_table(cfg, q_rows)
+    ck, sk = cos_sin_table(cfg, kr)
+    qs = rotate(q[q_rows], cq[:, None, :], sq[:, None, :])
+    ks = rotate(k[kr], ck[:, None, :], sk[:, None, :])
+    r = sink_attention_backward(qs, ks, v[kr], sinks, scale, q_rows, kr, window, dout[q_rows], with_noise=True)
+    out["dq"] = rotate_transpose(r[2], cq[:, None, :], sq[:, None, :])
+    nz_q = np.sqrt(_rotate_noise(r[6]["dq"], cq[:, None, :], sq[:, None, :]))
+    # dk, dv: every query that sees a key in [key_lo, key_hi), each with all keys it sees
+    q_hi = S - 1 if window <= 0 else min(S - 1, key_hi - 1 + window - 1)
+    qr = np.arange(key_lo, q_hi + 1)
+    klo = 0 if window <= 0 else max(0, key_lo - window + 1)
+    kr = np.arange(klo, q_hi + 1)
+    cq, sq = cos_sin_table(cfg, qr)
+    ck, sk = cos_sin_table(cfg, kr)
+    qs = rotate(q[qr], cq[:, None, :], sq[:, None, :])
+    ks = rotate(k[kr], ck[:, None, :], sk[:, None, :])
+    r = sink_attention_backward(qs, ks, v[kr], sinks, scale, qr, kr, window, dout[qr], with_noise=True)
+    sel = slice(key_lo - klo, key_hi - klo)
+    ck, sk = ck[sel], sk[sel]
+    out["dk"] = rotate_transpose(r[3][sel], ck[:, None, :], sk[:, None, :])
+    out["dv"] = r[4][sel]
+    out["noise"] = {"dq": nz_q,
+                    "dk": np.sqrt(_rotate_noise(r[6]["dk"][sel], ck[:, None, :], sk[:, None, :])),
+                    "dv": np.sqrt(r[6]["dv"][sel])}
+    return out

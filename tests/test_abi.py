@@ -184,3 +184,52 @@ def test_prefill_ex_rejects_unknown_k_rotation(lib):
     st = lib.gptoss_attn_prefill_ex(ctypes.byref(d), P, S3, P, K3, P, K3, P, 0.125, 0, P, 4096, 64, P, S3, P,
                                     1 << 30, 9, None)
     assert st == ERR_SHAPE
+
+
+def _desc_bshd(B=2, S=128):
+    return SeqDesc(0, B, S, S, None, 64, 8, 64)
+
+
+def _backward(lib, desc, **kw):
+    a = dict(q=P, qs=I64x3(128 * 64 * 64, 64 * 64, 64), k=P, ks=I64x3(128 * 8 * 64, 8 * 64, 64), v=P,
+             vs=I64x3(128 * 8 * 64, 8 * 64, 64), sinks=P, scale=0.125, window=0, table=P, rows=128, rd=64,
+             out=P, os=I64x3(128 * 64 * 64, 64 * 64, 64), dout=P, dos=I64x3(128 * 64 * 64, 64 * 64, 64), lse=P,
+             dq=P, dk=P, dv=P, ds=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.gptoss_attn_prefill_backward(ctypes.byref(desc) if desc is not None else None, a["q"], a["qs"],
+                                            a["k"], a["ks"], a["v"], a["vs"], a["sinks"], a["scale"], a["window"],
+                                            a["table"], a["rows"], a["rd"], a["out"], a["os"], a["dout"], a["dos"],
+                                            a["lse"], a["dq"], a["dk"], a["dv"], a["ds"], a["ws"], a["wsb"], None)
+
+
+def test_backward_argument_errors(lib):
+    d = _desc_bshd()
+    assert _backward(lib, None) == ERR_NULL
+    assert _backward(lib, _desc_bshd(), ds=None) == ERR_NULL
+    assert _backward(lib, d, dout=None) == ERR_NULL
+    assert _backward(lib, d, lse=None) == ERR_NULL
+    assert _backward(lib, d, window=-1) == ERR_SHAPE
+    assert _backward(lib, d, scale=0.0) == ERR_SHAPE
+    assert _backward(lib, d, rows=100) == ERR_SHAPE                     # table shorter than the sequence
+    assert _backward(lib, d, dos=I64x3(128 * 64 * 64, 64 * 64, 65)) == ERR_UNSUPPORTED
+    assert _backward(lib, d, lse=ctypes.c_void_p(0x10004)) == ERR_UNSUPPORTED
+    assert _backward(lib, d, wsb=16) == ERR_WORKSPACE
+    assert _backward(lib, SeqDesc(0, 2, 128, 128, None, 64, 8, 128)) == ERR_UNSUPPORTED   # head_dim 128
+
+
+def test_backward_workspace_size(lib):
+    d = _desc_bshd(4, 4096)
+    T = 4 * 4096
+    assert lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(d)) == T * 64 * 64 * 2 + T * 8 * 64 * 2 + 2 * T * 64 * 4
+    t = SeqDesc(1, 16, 65171, 8179, P, 64, 8, 64)
+    ws = lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(t))
+    assert ws >= 65171 * (64 * 64 * 2 + 8 * 64 * 2 + 2 * 64 * 4) + ((65171 + 31) // 32 + 16) * 8
+    assert lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(SeqDesc(0, 1, 8, 8, None, 60, 8, 64))) == 0
+
+
+def test_prefill_lse_requires_lse(lib):
+    d = _desc_bshd()
+    st = lib.gptoss_attn_prefill_lse(ctypes.byref(d), P, I64x3(128 * 64 * 64, 64 * 64, 64), P,
+                                     I64x3(128 * 8 * 64, 8 * 64, 64), P, I64x3(128 * 8 * 64, 8 * 64, 64), P, 0.125, 0,
+                                     P, 128, 64, P, I64x3(128 * 64 * 64, 64 * 64, 64), None, P, 1 << 30, None)
+    assert st == ERR_NULL

@@ -166,3 +166,31 @@ def test_backward_special_sinks(table):
         _check((o, lse) + tuple(grads), ref, f"sinks={val}")
         if val == -np.inf:
             assert torch.all(grads[3] == 0)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_backward_full_size_sampled(table, window):
+    """The benchmark's configuration (dense B=4 S=4096, both layers, the same inputs and
+    dO as bench.py): dq on 32 sampled query rows and dk, dv on whole 64-key tiles,
+    of batch 3, against the oracle's exact gradients at those rows and keys."""
+    inp = wl.dense()
+    dout = wl.grad_out(inp.q.shape, 7)
+    tab = gx.rope_table(4096)
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    say(f"[gpu] backward full size B=4 S=4096 W={window}")
+    o, lse = gx.attn_prefill_lse(q, k, v, s, window=window, table=tab)
+    dq, dk, dv, ds = gx.attn_prefill_backward(q, k, v, s, o, dout.cuda(), lse, window=window, table=tab)
+    torch.cuda.synchronize()
+    b = 3
+    extra = torch.randperm(4096, generator=torch.Generator().manual_seed(17))[:24].tolist()
+    rows = sorted(set([0, 1, 31, 32, 63, 64, 2047, 4095] + extra))
+    f64 = lambda t: t[b].double().numpy()
+    tiles = [(4032, 4096)] + ([(2048, 2112), (0, 64)] if window else [])
+    for lo, hi in tiles:
+        ref = oracle.prefill_backward_rows(f64(inp.q), f64(inp.k), f64(inp.v), np64(inp.sinks), TAU, window,
+                                           f64(dout), rows, lo, hi, CFG)
+        n = ref["noise"]
+        _assert_all([grad_close(dq[b, rows], ref["dq"], n["dq"], f"W={window} dq rows"),
+                     grad_close(dk[b, lo:hi], ref["dk"], n["dk"], f"W={window} dk keys {lo}..{hi - 1}"),
+                     grad_close(dv[b, lo:hi], ref["dv"], n["dv"], f"W={window} dv keys {lo}..{hi - 1}")],
+                    f"full size W={window}")

@@ -213,3 +213,20 @@ def test_noise_scales_single_key_closed_form():
         assert np.isclose(n["dsinks"][h], (1 - p) * np.sqrt(E), rtol=1e-11)
         assert np.isclose(n["m_dsinks"][h], abs((1 - p) * p * dvd), rtol=1e-11)
     assert np.allclose(n["dv"][0, 0, 0], np.sqrt((pv[:, None] ** 2 * dout[0, 0] ** 2).sum(0)), rtol=1e-11)
+
+
+@pytest.mark.parametrize("window", [0, 6])
+def test_rows_equal_the_whole_problem(window):
+    """prefill_backward_rows (selected query rows and a key range, sub-problems only)
+    equals the matching entries of the full backward."""
+    B, S, hq, hkv, d = 1, 40, 16, 2, 64
+    q, k, v, sinks, dout = _inputs(B, S, hq, hkv, d, 51 + window)
+    full = oracle.prefill_bshd_backward(q, k, v, sinks, TAU, window, dout, CFG, with_noise=True)
+    rows = [0, 3, 17, 39]
+    part = oracle.prefill_backward_rows(q[0], k[0], v[0], sinks, TAU, window, dout[0], rows, 20, 31, CFG)
+    assert np.allclose(part["dq"], full["dq"][0, rows], rtol=1e-12, atol=1e-13)
+    assert np.allclose(part["dk"], full["dk"][0, 20:31], rtol=1e-12, atol=1e-13)
+    assert np.allclose(part["dv"], full["dv"][0, 20:31], rtol=1e-12, atol=1e-13)
+    assert np.allclose(part["noise"]["dq"], full["noise"]["dq"][0, rows], rtol=1e-12)
+    assert np.allclose(part["noise"]["dk"], full["noise"]["dk"][0, 20:31], rtol=1e-12)
+    assert np.allclose(part["noise"]["dv"], full["noise"]["dv"][0, 20:31], rtol=1e-12)
