@@ -366,7 +366,7 @@ size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc) 
              round_up((size_t)thd_items(desc, kBackwardNK) * sizeof(int2)) + kAlign;
   bytes += round_up(T * hq * kHeadDim * sizeof(uint16_t));    // rotated q
   bytes += round_up(T * hkv * kHeadDim * sizeof(uint16_t));   // rotated k
-  bytes += 2 * round_up(T * hq * sizeof(float));              // D = <dO, o> and lse (log2), head-major
+  bytes += round_up(T * hq * 2 * sizeof(float));              // (lse in log2 units, D = <dO, o>), head-major
   return bytes;
 }
 
@@ -437,9 +437,7 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   ws += round_up((size_t)T * hq * kHeadDim * sizeof(uint16_t));
   uint16_t* krot = reinterpret_cast<uint16_t*>(ws);
   ws += round_up((size_t)T * hkv * kHeadDim * sizeof(uint16_t));
-  p.dd = reinterpret_cast<float*>(ws);
-  ws += round_up((size_t)T * hq * sizeof(float));
-  p.lse2 = reinterpret_cast<float*>(ws);
+  p.ld = reinterpret_cast<float*>(ws);
   p.tokens = T;
 
   if (table) {

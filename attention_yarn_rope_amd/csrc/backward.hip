@@ -13,15 +13,16 @@
 //
 // Kernels, in launch order (the caller's q and k are rotated into the
 // workspace first by the standalone rotation kernel):
-//   bwd_pre_kernel     D for every (token, query head): 8 lanes per row.
-//   bwd_sink_kernel    dsigma per head: one work group per head sums its rows
-//                      in a fixed order (no atomics, reproducible).
 //   bwd_dq_kernel      work item (sequence, KV head, 32 query positions): like
 //                      the forward, every K/V tile is staged in LDS once for
 //                      the 8 query heads; per tile a wave runs S^T = K Q^T and
 //                      dP^T = V dO^T (16 + 16 MFMAs), forms dS^T in registers and
 //                      accumulates dQ^T += K^T dS^T (16 MFMAs, K^T read from
-//                      the row-major K tile with ds_read_b64_tr_b16).
+//                      the row-major K tile with ds_read_b64_tr_b16). It also
+//                      forms D = <dO, o> per row and writes D and lse
+//                      head-major for the kernels after it.
+//   bwd_sink_kernel    dsigma per head: one work group per head sums its rows
+//                      in a fixed order (no atomics, reproducible).
 //   bwd_dkdv_kernel    work item (sequence, KV head, 64 keys): K and V of the
 //                      tile stay in registers as MFMA fragments; each of 4 waves
 //                      takes 2 of the 8 query heads and walks every 32-query
@@ -45,59 +46,23 @@ constexpr int QS = 80;           // LDS row stride of a wave's q / dO tile (dk/d
 
 __device__ __forceinline__ uint2 ldg8(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
-// ---------------------------------------------------------------------------
-// D = <dO, o> per (token, query head), and lse in log2 units, both written
-// head-major [Hq, tokens] so the kernels below read a head's consecutive rows
-// contiguously. Work group: 32 tokens of one head, 8 lanes per row.
-// ---------------------------------------------------------------------------
-template <bool THD>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BackwardParams p) {
-  const int Hq = p.num_kv_heads * kGroup;
-  const int h = blockIdx.y;
-  const int64_t t = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int c = threadIdx.x & 7;
-  if (t >= p.tokens) return;   // whole 8-lane groups leave together
-  bool valid = true;
-  int64_t oo, od;
-  if (THD) {
-    valid = t < __ldg(p.cu_seqlens + p.batch);   // tokens after the last sequence belong to none
-    oo = t * p.o_st + h * p.o_sh;
-    od = t * p.do_st + h * p.do_sh;
-  } else {
-    const int64_t b = t / p.seqlen, s = t - b * p.seqlen;
-    oo = b * p.o_sb + s * p.o_st + h * p.o_sh;
-    od = b * p.do_sb + s * p.do_st + h * p.do_sh;
-  }
-  float acc = 0.0f;
-  if (valid) {
-    const uint4 a = ldg16(p.o + oo + 8 * c), d = ldg16(p.dout + od + 8 * c);
-    const uint32_t* pa = reinterpret_cast<const uint32_t*>(&a);
-    const uint32_t* pd = reinterpret_cast<const uint32_t*>(&d);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc += bf16_lo(pa[i]) * bf16_lo(pd[i]) + bf16_hi(pa[i]) * bf16_hi(pd[i]);
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  if (c == 0) {
-    const float l = valid ? p.lse[t * Hq + h] : -INFINITY;
-    p.dd[(int64_t)h * p.tokens + t] = acc;
-    // a row without any term (lse = -inf) gets +inf: its probabilities exp2(x - lse2) are 0
-    p.lse2[(int64_t)h * p.tokens + t] = (l > -INFINITY) ? l * kLog2e : INFINITY;
-  }
-}
-
 // dsigma_h = - sum over the head's rows of exp(sigma_h - lse) * D, one work
 // group per head, each thread summing a fixed stride of rows, then a tree.
+// D and lse (log2 units) come head-major from the dq kernel; packed tokens
+// after the last sequence belong to none and are left out.
+template <bool THD>
 __global__ __launch_bounds__(256) void bwd_sink_kernel(BackwardParams p) {
   __shared__ float part[256];
   const int h = blockIdx.x;
   const float sig2 = p.sinks[h] * kLog2e;
-  const float* l2 = p.lse2 + (int64_t)h * p.tokens;
-  const float* dd = p.dd + (int64_t)h * p.tokens;
+  const float2* ld = reinterpret_cast<const float2*>(p.ld) + (int64_t)h * p.tokens;
+  const int64_t rows = THD ? (int64_t)min(max(__ldg(p.cu_seqlens + p.batch), 0), p.seqlen) : p.tokens;
   float acc = 0.0f;
   if (sig2 > -INFINITY) {
-    for (int64_t t = threadIdx.x; t < p.tokens; t += 256) acc -= __builtin_amdgcn_exp2f(sig2 - l2[t]) * dd[t];
+    for (int64_t t = threadIdx.x; t < rows; t += 256) {
+      const float2 x = ld[t];
+      acc -= __builtin_amdgcn_exp2f(sig2 - x.x) * x.y;
+    }
   }
   part[threadIdx.x] = acc;
   __syncthreads();
@@ -140,7 +105,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int item = blockIdx.x / Hkv;
   const int g = blockIdx.x - item * Hkv;
   int j, L, ts;
-  int64_t row0, bq_, bk_, bv_, bd_;
+  int64_t row0, bq_, bk_, bv_, bd_, bo_;
   if (THD) {
     if (item >= __ldg(p.count_q)) return;
     const int2 w = p.work_q[item];
@@ -148,14 +113,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int n = min(max(w.x, 0), p.batch - 1);
     ts = min(max(__ldg(p.cu_seqlens + n), 0), p.seqlen);
     L = min(max(__ldg(p.cu_seqlens + n + 1), ts), p.seqlen) - ts;
-    row0 = 0; bq_ = bk_ = bv_ = bd_ = 0;
+    row0 = 0; bq_ = bk_ = bv_ = bd_ = bo_ = 0;
   } else {
     const int r = item / p.batch, b = item - r * p.batch;
     j = p.q_blocks - 1 - r;   // most keys first
     ts = 0;
     L = p.seqlen;
     row0 = (int64_t)b * p.seqlen;
-    bq_ = b * p.q_sb; bk_ = b * p.k_sb; bv_ = b * p.v_sb; bd_ = b * p.do_sb;
+    bq_ = b * p.q_sb; bk_ = b * p.k_sb; bv_ = b * p.v_sb; bd_ = b * p.do_sb; bo_ = b * p.o_sb;
   }
   const int q0 = j * BQ;
   if (j < 0 || q0 >= L) return;
@@ -188,7 +153,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   if (ntiles > 0) load_tile(0);
   // q~ and dO of the wave's 32 rows as B-operand fragments (lane = query column,
-  // 8 consecutive dims), and each column's lse (log2 units) and D.
+  // 8 consecutive dims); each column's D = <dO, o> (the 16 dims of a lane, then
+  // summed over the column's 4 lanes) and lse in log2 units (+inf for a row
+  // without any term: its probabilities are 0). Both are also written head-major
+  // to the workspace for the dk / dv kernels and the sink gradient, which run
+  // after this kernel.
   int qpos[2];
   bf16x8_t qf[2][2], df[2][2];
   float lse2[2], dd[2];
@@ -198,13 +167,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int pos = min(qpos[cb], qlast);
     const bf16_t* qp = p.q + bq_ + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh + 8 * grp;
     const bf16_t* dp = p.dout + bd_ + (int64_t)(ts + pos) * p.do_st + (int64_t)head * p.do_sh + 8 * grp;
+    const bf16_t* op = p.o + bo_ + (int64_t)(ts + pos) * p.o_st + (int64_t)head * p.o_sh + 8 * grp;
+    const uint4 d0 = ldg16(dp), d1 = ldg16(dp + 32), o0 = ldg16(op), o1 = ldg16(op + 32);
     qf[cb][0] = as_bf16x8(ldg16(qp));
     qf[cb][1] = as_bf16x8(ldg16(qp + 32));
-    df[cb][0] = as_bf16x8(ldg16(dp));
-    df[cb][1] = as_bf16x8(ldg16(dp + 32));
-    const int64_t rr = (int64_t)head * p.tokens + row0 + ts + pos;
-    lse2[cb] = p.lse2[rr];
-    dd[cb] = p.dd[rr];
+    df[cb][0] = as_bf16x8(d0);
+    df[cb][1] = as_bf16x8(d1);
+    const float l = p.lse[(row0 + ts + pos) * Hq + head];
+    lse2[cb] = (l > -INFINITY) ? l * kLog2e : INFINITY;
+    float dot = 0.0f;
+    const uint32_t* pd0 = reinterpret_cast<const uint32_t*>(&d0);
+    const uint32_t* pd1 = reinterpret_cast<const uint32_t*>(&d1);
+    const uint32_t* po0 = reinterpret_cast<const uint32_t*>(&o0);
+    const uint32_t* po1 = reinterpret_cast<const uint32_t*>(&o1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dot += bf16_lo(pd0[i]) * bf16_lo(po0[i]) + bf16_hi(pd0[i]) * bf16_hi(po0[i]) +
+             bf16_lo(pd1[i]) * bf16_lo(po1[i]) + bf16_hi(pd1[i]) * bf16_hi(po1[i]);
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    dd[cb] = dot;
+    if (grp == 0 && qpos[cb] <= qlast) {
+      const int64_t rr = (int64_t)head * p.tokens + row0 + ts + pos;
+      reinterpret_cast<float2*>(p.ld)[rr] = make_float2(lse2[cb], dot);
+    }
   }
 
   f32x4_t acc[4][2];
@@ -309,20 +295,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 }
 
 // ---------------------------------------------------------------------------
-// dv (PART 0) or dk (PART 1): one work group of 4 waves per (sequence, KV head
-// g, 64 keys); wave w owns query heads 8 g + 2 w and 8 g + 2 w + 1. The two
-// gradients are separate launches so each wave holds one 64-key x 64-dim fp32
-// accumulator (64 VGPRs) and two waves fit on a SIMD; S = Q K^T is formed in
-// both (its 16 MFMAs per step are the price).
+// dk and dv: one work group of 4 waves per (sequence, KV head g, 64 keys). Wave
+// w takes the 32 keys t0 + 32 (w & 1) .. + 31 and query heads 8 g + 4 (w >> 1)
+// .. + 3, and holds fp32 dK^T and dV^T for its keys (64 VGPRs); the two waves of
+// a key half are summed through LDS at the end.
 // ---------------------------------------------------------------------------
-constexpr int kKvLds = 4 * 16 * 64 * 16;   // cross-wave sum: 4 waves x 16 fragments x 64 lanes x 16 B
-static_assert(4 * BQ * QS * 2 <= kKvLds, "per-wave transpose tiles fit in the reduction space");
+constexpr int kKvLds = 4 * 2 * BQ * QS * 2;   // per-wave q and dO tiles (bytes); the final sum reuses them
+static_assert(4 * 8 * 64 * 16 <= kKvLds, "the cross-wave sum of one tensor fits in the tiles' space");
 
-template <bool THD, bool ROT, int PART>
+template <bool THD, bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) char lds_raw[kKvLds];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_ld[4 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
+  const int kh = wave & 1, hp = wave >> 1;
   const int Hkv = p.num_kv_heads;
   const int item = blockIdx.x / Hkv;
   const int g = blockIdx.x - item * Hkv;
@@ -347,200 +334,188 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int t0 = jt * NK;
   if (jt < 0 || t0 >= L) return;
   const int tlast = min(t0 + NK, L) - 1;
+  const int k0 = t0 + 32 * kh;   // the wave's first key
   const int W = p.window;
   const uint32_t weff = (W > 0) ? (uint32_t)W : 0x7FFFFFFFu;
   const int qhi = (W > 0) ? min(L - 1, tlast + W - 1) : L - 1;   // last query that sees a key of the tile
   const float sl = p.scale_log2;
 
-  // K (and, for dk, V) of the tile as B-operand fragments: lane = key column, 8 consecutive dims
-  bf16x8_t kf[4][2], vf[4][2];
+  // K and V of the wave's 32 keys as B-operand fragments: lane = key column, 8 consecutive dims
+  bf16x8_t kf[2][2], vf[2][2];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int key = min(t0 + kb * 16 + col, tlast);
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = min(k0 + kb * 16 + col, tlast);
     const bf16_t* kp = p.k + bk_ + (int64_t)(ts + key) * p.k_st + (int64_t)g * p.k_sh + 8 * grp;
+    const bf16_t* vp = p.v + bv_ + (int64_t)(ts + key) * p.v_st + (int64_t)g * p.v_sh + 8 * grp;
     kf[kb][0] = as_bf16x8(ldg16(kp));
     kf[kb][1] = as_bf16x8(ldg16(kp + 32));
-    if (PART == 1) {
-      const bf16_t* vp = p.v + bv_ + (int64_t)(ts + key) * p.v_st + (int64_t)g * p.v_sh + 8 * grp;
-      vf[kb][0] = as_bf16x8(ldg16(vp));
-      vf[kb][1] = as_bf16x8(ldg16(vp + 32));
-    }
+    vf[kb][0] = as_bf16x8(ldg16(vp));
+    vf[kb][1] = as_bf16x8(ldg16(vp + 32));
   }
-  f32x4_t acc[4][4];   // [d block][key block]: element r = dim 16*db + 4*grp + r, key col (dV^T or dK^T)
+  f32x4_t dkt[4][2], dvt[4][2];   // [d block][key block]: element r = dim 16*db + 4*grp + r, key col
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 2; ++b) dkt[a][b] = dvt[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // this wave's tile [32 queries][QS] for the transpose reads: dO (dv) or q (dk)
-  bf16_t* lt = reinterpret_cast<bf16_t*>(lds_raw) + wave * (BQ * QS);
+  // the wave's q and dO tiles [32 queries][QS] for the transpose reads
+  bf16_t* lq = reinterpret_cast<bf16_t*>(lds_raw) + wave * (2 * BQ * QS);
+  bf16_t* ldo = lq + BQ * QS;
+  uint32_t* lld = lds_ld + wave * 64;
 
-  // Steps: every block of 32 queries that can see the tile, once per head of the
-  // wave (head 8 g + 2 wave + hh). In dv the global loads of the next step are in
-  // flight while a step computes.
-  const int qb_lo = t0 / BQ;
   // Rows are read through buffer ranges that end with the sequence: rows past it
   // read as zeros (their dO is 0, so they add nothing to dV or dK) and need no
-  // clamps; one 32-bit offset per load. The ranges of the wave's two heads are
-  // wave-uniform.
+  // clamps; one 32-bit offset per load. Each fetch builds its head's ranges in
+  // scalar registers (the head is wave-uniform).
   const int32_t qrow_b = (int32_t)p.q_st * 2, drow_b = (int32_t)p.do_st * 2;   // < 2^31 / (L + 32): host check
-  __amdgpu_buffer_rsrc_t rq[2], rd[2], rl[2], rdd[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int head = g * kGroup + 2 * wave + hh;
-    rq[hh] = make_rsrc(p.q + bq_ + (int64_t)ts * p.q_st + (int64_t)head * p.q_sh, (L - 1) * qrow_b + 2 * kHeadDim);
-    rd[hh] = make_rsrc(p.dout + bd_ + (int64_t)ts * p.do_st + (int64_t)head * p.do_sh, (L - 1) * drow_b + 2 * kHeadDim);
-    rl[hh] = make_rsrc(p.lse2 + (int64_t)head * p.tokens + row0 + ts, L * 4);
-    rdd[hh] = make_rsrc(p.dd + (int64_t)head * p.tokens + row0 + ts, L * 4);
-  }
-  struct Fetch { uint4 qa[2][2], da[2][2]; float l2[2][4], dd[2][4]; };
-  // hh is a constant at every call (the calls are unrolled), so the ranges stay scalar
+  struct Fetch { uint4 qa[2][2], da[2][2]; uint32_t ld; };
   auto fetch = [&](int qb, int hh, Fetch& f) __attribute__((always_inline)) {
     const int q0 = qb * BQ;
-    const __amdgpu_buffer_rsrc_t bq = rq[hh], bd = rd[hh], bl = rl[hh], bdd = rdd[hh];
+    const int head = g * kGroup + 4 * hp + hh;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(p.q + bq_ + (int64_t)ts * p.q_st + (int64_t)head * p.q_sh, (L - 1) * qrow_b + 2 * kHeadDim);
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(p.dout + bd_ + (int64_t)ts * p.do_st + (int64_t)head * p.do_sh, (L - 1) * drow_b + 2 * kHeadDim);
 #pragma unroll
     for (int qm = 0; qm < 2; ++qm) {
       // q~ and dO rows as A-operand fragments (lane = query row, 8 consecutive dims)
       const uint32_t qo = (uint32_t)((q0 + qm * 16 + col) * qrow_b + 16 * grp);
       const uint32_t dof = (uint32_t)((q0 + qm * 16 + col) * drow_b + 16 * grp);
-      f.qa[qm][0] = ldb16(bq, qo); f.qa[qm][1] = ldb16(bq, qo + 64);
-      f.da[qm][0] = ldb16(bd, dof); f.da[qm][1] = ldb16(bd, dof + 64);
-      // lse (log2 units) and D of the lane's queries q0 + 16 qm + 4 grp + e
-      const uint32_t lo = (uint32_t)((q0 + qm * 16 + 4 * grp) * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f.l2[qm][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bl, lo + 4 * e, 0, 0));
-        if (PART == 1) f.dd[qm][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bdd, lo + 4 * e, 0, 0));
-      }
+      f.qa[qm][0] = ldb16(rq, qo); f.qa[qm][1] = ldb16(rq, qo + 64);
+      f.da[qm][0] = ldb16(rd, dof); f.da[qm][1] = ldb16(rd, dof + 64);
     }
+    // (lse, D) of the 32 queries: one float per lane, lane = 2 query + which
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.ld + 2 * ((int64_t)head * p.tokens + row0 + ts), L * 8);
+    f.ld = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)((2 * q0 + lane) * 4), 0, 0);
   };
-  auto step = [&](int qb, const Fetch& f) __attribute__((always_inline)) {
+  auto step = [&](int qb, int hh, const Fetch& f) __attribute__((always_inline)) {
     const int q0 = qb * BQ;
-    const bool full = (q0 >= t0 + NK - 1) && (W == 0 || q0 + BQ - 1 - t0 < W);
-    {
-      const uint4 (&qa)[2][2] = f.qa;
-      const uint4 (&da)[2][2] = f.da;
-      const float (&lse2)[2][4] = f.l2;
-      const float (&dd)[2][4] = f.dd;
-      // the previous step's transpose reads are complete before the tile is rewritten
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
+    const bool full = (q0 >= k0 + 31) && (W == 0 || q0 + BQ - 1 - k0 < W);
+    // the previous step's transpose reads are complete before the tiles are rewritten
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int qm = 0; qm < 2; ++qm)
+    for (int qm = 0; qm < 2; ++qm)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          *reinterpret_cast<uint4*>(lt + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = PART ? qa[qm][ks] : da[qm][ks];
-
-      // Per 16-query half qm: S = Q K^T (and dP = dO V^T) with [kb] element e = query
-      // q0 + 16 qm + 4 grp + e, key t0 + 16 kb + col; then P (dv) or dS = P (dP - D) (dk),
-      // packed as the B operand over the 32 queries (elements 4 qm .. 4 qm + 3)
-      uint32_t bw[4][4];   // [kb][word]
+      for (int ks = 0; ks < 2; ++ks) {
+        *reinterpret_cast<uint4*>(lq + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = f.qa[qm][ks];
+        *reinterpret_cast<uint4*>(ldo + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = f.da[qm][ks];
+      }
+    lld[lane] = f.ld;
+    // Per 16-query half qm: S = Q K^T and dP = dO V^T ([kb] element e = query
+    // q0 + 16 qm + 4 grp + e, key k0 + 16 kb + col), then P and dS = P (dP - D),
+    // packed as B operands over the 32 queries (elements 4 qm .. 4 qm + 3)
+    uint32_t pw[2][4], dw[2][4];   // [kb][word]
 #pragma unroll
-      for (int qm = 0; qm < 2; ++qm) {
-        f32x4_t s_[4], dp_[4];
+    for (int qm = 0; qm < 2; ++qm) {
+      // (lse, D) of the lane's queries q0 + 16 qm + 4 grp + e, e = 0..3 (a wave's LDS
+      // operations complete in order: the words written above are there)
+      const uint4 x0 = *reinterpret_cast<const uint4*>(lld + 32 * qm + 8 * grp);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(lld + 32 * qm + 8 * grp + 4);
+      const float l2[4] = {__uint_as_float(x0.x), __uint_as_float(x0.z), __uint_as_float(x1.x), __uint_as_float(x1.z)};
+      const float dd[4] = {__uint_as_float(x0.y), __uint_as_float(x0.w), __uint_as_float(x1.y), __uint_as_float(x1.w)};
+      f32x4_t s_[2], dp_[2];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          s_[kb] = mfma16(as_bf16x8(qa[qm][1]), kf[kb][1], mfma16(as_bf16x8(qa[qm][0]), kf[kb][0], z));
-          if (PART == 1)
-            dp_[kb] = mfma16(as_bf16x8(da[qm][1]), vf[kb][1], mfma16(as_bf16x8(da[qm][0]), vf[kb][0], z));
-        }
-        if (!full) {
+      for (int kb = 0; kb < 2; ++kb) {
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        s_[kb] = mfma16(as_bf16x8(f.qa[qm][1]), kf[kb][1], mfma16(as_bf16x8(f.qa[qm][0]), kf[kb][0], z));
+        dp_[kb] = mfma16(as_bf16x8(f.da[qm][1]), vf[kb][1], mfma16(as_bf16x8(f.da[qm][0]), vf[kb][0], z));
+      }
+      if (!full) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int qq = q0 + qm * 16 + 4 * grp + e, key = t0 + kb * 16 + col;
-              s_[kb][e] = ((uint32_t)(qq - key) < weff) ? s_[kb][e] : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          float x[4];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[kb][e], sl, -lse2[qm][e]));
-            x[e] = (PART == 1) ? pr * (dp_[kb][e] - dd[qm][e]) : pr;
+            const int qq = q0 + qm * 16 + 4 * grp + e, key = k0 + kb * 16 + col;
+            s_[kb][e] = ((uint32_t)(qq - key) < weff) ? s_[kb][e] : -INFINITY;
           }
-          bw[kb][2 * qm] = pack_bf16x2(x[0], x[1]);
-          bw[kb][2 * qm + 1] = pack_bf16x2(x[2], x[3]);
-        }
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-      // dV^T += dO^T P (dv) or dK^T += Q^T dS (dk), the first operand read transposed from the tile
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int off = (4 * grp + (col >> 2)) * QS + 16 * db + 4 * (col & 3);
-        const uint2 lo = lds_read_tr16(lt + off), hi = lds_read_tr16(lt + off + 16 * QS);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[4], dv_[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          acc[db][kb] = mfma16(a, __builtin_bit_cast(bf16x8_t, make_uint4(bw[kb][0], bw[kb][1], bw[kb][2], bw[kb][3])),
-                               acc[db][kb]);
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[kb][e], sl, -l2[e]));
+          dv_[e] = pv[e] * (dp_[kb][e] - dd[e]);
+        }
+        pw[kb][2 * qm] = pack_bf16x2(pv[0], pv[1]);
+        pw[kb][2 * qm + 1] = pack_bf16x2(pv[2], pv[3]);
+        dw[kb][2 * qm] = pack_bf16x2(dv_[0], dv_[1]);
+        dw[kb][2 * qm + 1] = pack_bf16x2(dv_[2], dv_[3]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T read transposed from the tiles)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int off = (4 * grp + (col >> 2)) * QS + 16 * db + 4 * (col & 3);
+      const uint2 dlo = lds_read_tr16(ldo + off), dhi = lds_read_tr16(ldo + off + 16 * QS);
+      const uint2 qlo = lds_read_tr16(lq + off), qhi2 = lds_read_tr16(lq + off + 16 * QS);
+      const bf16x8_t a_do = __builtin_bit_cast(bf16x8_t, make_uint4(dlo.x, dlo.y, dhi.x, dhi.y));
+      const bf16x8_t a_q = __builtin_bit_cast(bf16x8_t, make_uint4(qlo.x, qlo.y, qhi2.x, qhi2.y));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        dvt[db][kb] = mfma16(a_do, __builtin_bit_cast(bf16x8_t, make_uint4(pw[kb][0], pw[kb][1], pw[kb][2], pw[kb][3])),
+                             dvt[db][kb]);
+        dkt[db][kb] = mfma16(a_q, __builtin_bit_cast(bf16x8_t, make_uint4(dw[kb][0], dw[kb][1], dw[kb][2], dw[kb][3])),
+                             dkt[db][kb]);
       }
     }
   };
-  // Query blocks are walked from the last one down: the work groups of one
-  // (sequence, KV head) run together on one XCD (consecutive work groups take
-  // consecutive KV heads, dealt round-robin over the 8 XCDs) and then read the
-  // same q / dO block at about the same time, so L2 serves the repeats.
-  const int qb_hi = qhi / BQ;
-  if (PART == 0) {
-    // dv holds two fetch buffers in turn: each step computes from one while the
-    // other receives the next step's rows, with no register copies between steps
-    Fetch fa, fb;
-    fetch(qb_hi, 0, fa);
-    for (int qb = qb_hi; qb >= qb_lo; --qb) {
-      fetch(qb, 1, fb);
-      step(qb, fa);
-      fetch(max(qb - 1, qb_lo), 0, fa);   // the last block fetches itself again: no branch
-      step(qb, fb);
-    }
-  } else {
-    // dk has no registers to spare for a second buffer: each step loads its own rows
-    for (int qb = qb_hi; qb >= qb_lo; --qb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        Fetch f;
-        fetch(qb, hh, f);
-        step(qb, f);
-      }
-    }
+
+  // Steps: every block of 32 queries that can see the tile, walked from the last
+  // one down, once per head of the wave. The work groups of one (sequence, KV
+  // head) run together on one XCD (consecutive work groups take consecutive KV
+  // heads, dealt round-robin over the 8 XCDs) and then read the same q / dO
+  // block at about the same time, so L2 serves the repeats. Two buffers of q /
+  // dO rows (and their lse and D) take turns: a step computes from one while
+  // the other receives the next step's rows (no register copies between steps).
+  const int qb_lo = t0 / BQ, qb_hi = qhi / BQ;
+  Fetch fa, fb;
+  fetch(qb_hi, 0, fa);
+  for (int qb = qb_hi; qb >= qb_lo; --qb) {
+    fetch(qb, 1, fb);
+    step(qb, 0, fa);
+    fetch(qb, 2, fa);
+    step(qb, 1, fb);
+    fetch(qb, 3, fb);
+    step(qb, 2, fa);
+    fetch(max(qb - 1, qb_lo), 0, fa);   // the last block fetches itself again: no branch
+    step(qb, 3, fb);
   }
 
-  // sum the 4 waves' partials through LDS; wave w finishes d blocks (w & 1, (w & 1) + 2)
-  // -- the rotation pairs dims i and i + 32 -- of key blocks 2 (w >> 1) and 2 (w >> 1) + 1
+  // sum the two waves of each key half through LDS (waves kh and kh + 2); wave w
+  // finishes d blocks (w >> 1, (w >> 1) + 2) -- the rotation pairs dims i and
+  // i + 32 -- of the key half w & 1
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds_raw);
-  const int pr = wave & 1, kh = wave >> 1;
-  __syncthreads();
+  const int pr = wave >> 1;
+#pragma unroll 1
+  for (int which = 0; which < 2; ++which) {
+    __syncthreads();
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) red[(wave * 16 + db * 4 + kb) * 64 + lane] = acc[db][kb];
-  __syncthreads();
+      for (int kb = 0; kb < 2; ++kb) red[(wave * 8 + db * 2 + kb) * 64 + lane] = which ? dvt[db][kb] : dkt[db][kb];
+    __syncthreads();
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int kb = 2 * kh + kk;
-    const int key = t0 + kb * 16 + col;
-    f32x4_t y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      y1 += red[(w * 16 + pr * 4 + kb) * 64 + lane];
-      y2 += red[(w * 16 + (pr + 2) * 4 + kb) * 64 + lane];
-    }
-    if (key > tlast) continue;
-    if (PART == 1) {
-      y1 *= p.scale;
-      y2 *= p.scale;
-      if (ROT) {
-        const bf16_t* tp = p.table + (int64_t)min(key, p.table_rows - 1) * kHeadDim + 16 * pr + 4 * grp;
-        rotate_back4(y1, y2, ldg8(tp), ldg8(tp + 32));
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = k0 + kb * 16 + col;
+      f32x4_t y1 = red[(kh * 8 + pr * 2 + kb) * 64 + lane] + red[((kh + 2) * 8 + pr * 2 + kb) * 64 + lane];
+      f32x4_t y2 = red[(kh * 8 + (pr + 2) * 2 + kb) * 64 + lane] + red[((kh + 2) * 8 + (pr + 2) * 2 + kb) * 64 + lane];
+      if (key > tlast) continue;
+      if (which == 0) {
+        y1 *= p.scale;
+        y2 *= p.scale;
+        if (ROT) {
+          const bf16_t* tp = p.table + (int64_t)min(key, p.table_rows - 1) * kHeadDim + 16 * pr + 4 * grp;
+          rotate_back4(y1, y2, ldg8(tp), ldg8(tp + 32));
+        }
       }
+      bf16_t* op = (which ? p.dv : p.dk) + ((row0 + ts + key) * Hkv + g) * kHeadDim + 16 * pr + 4 * grp;
+      *reinterpret_cast<uint2*>(op) = pack4(y1);
+      *reinterpret_cast<uint2*>(op + 32) = pack4(y2);
     }
-    bf16_t* op = (PART == 1 ? p.dk : p.dv) + ((row0 + ts + key) * Hkv + g) * kHeadDim + 16 * pr + 4 * grp;
-    *reinterpret_cast<uint2*>(op) = pack4(y1);
-    *reinterpret_cast<uint2*>(op + 32) = pack4(y2);
   }
 }
 
@@ -552,15 +527,13 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* x, int32_t n, floa
 template <bool THD, bool ROT>
 hipError_t launch_all(const BackwardParams& p, hipStream_t stream) {
   const int Hq = p.num_kv_heads * kGroup;
-  const int64_t tokens = THD ? (int64_t)p.seqlen : (int64_t)p.batch * p.seqlen;
-  hipLaunchKernelGGL(bwd_pre_kernel<THD>, dim3((uint32_t)((tokens + 31) / 32), Hq), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(bwd_sink_kernel, dim3(Hq), dim3(256), 0, stream, p);
   const int64_t rep = THD ? 1 : p.batch;
+  // dq first: it also writes D and lse (log2 units) for the kernels after it
   hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)), dim3(512), 0,
                      stream, p);
-  const dim3 kv_grid((uint32_t)(p.k_tiles * rep * p.num_kv_heads));
-  hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT, 0>), kv_grid, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT, 1>), kv_grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(bwd_sink_kernel<THD>, dim3(Hq), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT>), dim3((uint32_t)(p.k_tiles * rep * p.num_kv_heads)), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -68,8 +68,8 @@ struct BackwardParams {
   const uint16_t* o; int64_t o_sb, o_st, o_sh;     // forward output
   const uint16_t* dout; int64_t do_sb, do_st, do_sh;
   const float* lse;              // [tokens, Hq] natural log, from the forward
-  float* lse2;                   // workspace [Hq, tokens]: lse in log2 units, +inf for rows without a gradient
-  float* dd;                     // workspace [Hq, tokens]: D = <dO, o>
+  float* ld;                     // workspace [Hq, tokens, 2]: per row lse in log2 units (+inf for a row
+                                 // without any term) and D = <dO, o>
   int64_t tokens;                // rows of the token-major tensors (BSHD batch * seqlen, THD seqlen)
   const float* sinks;
   float* dsinks;                 // [Hq]
