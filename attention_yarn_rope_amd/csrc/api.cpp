@@ -363,7 +363,7 @@ size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc) 
   size_t bytes = 0;
   if (desc->layout == GPTOSS_THD)
     bytes += round_up((size_t)thd_items(desc, kPrefillBQ) * sizeof(int2)) + kAlign +
-             round_up((size_t)thd_items(desc, kBackwardNK) * sizeof(int2)) + kAlign;
+             round_up((size_t)thd_items(desc, kBackwardKT) * sizeof(int2)) + kAlign;
   bytes += round_up(T * hq * kHeadDim * sizeof(uint16_t));    // rotated q
   bytes += round_up(T * hkv * kHeadDim * sizeof(uint16_t));   // rotated k
   bytes += round_up(T * hq * 2 * sizeof(float));              // (lse in log2 units, D = <dO, o>), head-major
@@ -414,7 +414,7 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   BackwardParams p;
   memset(&p, 0, sizeof p);
   if (thd) {
-    const int32_t nq = thd_items(desc, kPrefillBQ), nk = thd_items(desc, kBackwardNK);
+    const int32_t nq = thd_items(desc, kPrefillBQ), nk = thd_items(desc, kBackwardKT);
     int2* wq = reinterpret_cast<int2*>(ws);
     ws += round_up((size_t)nq * sizeof(int2));
     int32_t* cq = reinterpret_cast<int32_t*>(ws);
@@ -425,13 +425,13 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
     ws += kAlign;
     st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, kPrefillBQ, nq, wq, cq, s), "THD schedule");
     if (st != GPTOSS_OK) return st;
-    st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, kBackwardNK, nk, wk, ck, s), "THD schedule");
+    st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, kBackwardKT, nk, wk, ck, s), "THD schedule");
     if (st != GPTOSS_OK) return st;
     p.work_q = wq; p.count_q = cq; p.q_blocks = nq;
     p.work_k = wk; p.count_k = ck; p.k_tiles = nk;
   } else {
     p.q_blocks = (desc->seqlen + kPrefillBQ - 1) / kPrefillBQ;
-    p.k_tiles = (desc->seqlen + kBackwardNK - 1) / kBackwardNK;
+    p.k_tiles = (desc->seqlen + kBackwardKT - 1) / kBackwardKT;
   }
   uint16_t* qrot = reinterpret_cast<uint16_t*>(ws);
   ws += round_up((size_t)T * hq * kHeadDim * sizeof(uint16_t));

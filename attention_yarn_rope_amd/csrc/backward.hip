@@ -19,18 +19,19 @@
 //                      dP^T = V dO^T (16 + 16 MFMAs), forms dS^T in registers and
 //                      accumulates dQ^T += K^T dS^T (16 MFMAs, K^T read from
 //                      the row-major K tile with ds_read_b64_tr_b16). It also
-//                      forms D = <dO, o> per row and writes D and lse
-//                      head-major for the kernels after it.
+//                      forms D = <dO, o> per row and writes (lse in log2
+//                      units, D) head-major for the kernels after it.
 //   bwd_sink_kernel    dsigma per head: one work group per head sums its rows
 //                      in a fixed order (no atomics, reproducible).
-//   bwd_dkdv_kernel    work item (sequence, KV head, 64 keys): K and V of the
-//                      tile stay in registers as MFMA fragments; each of 4 waves
-//                      takes 2 of the 8 query heads and walks every 32-query
-//                      block that can see the tile: S = Q K^T and dP = dO V^T
-//                      (16 + 16 MFMAs), then dV^T += dO^T P and dK^T += Q^T dS
-//                      (16 + 16 MFMAs; dO^T and Q^T through a per-wave LDS
-//                      tile and transpose reads). The 4 waves' partial dK, dV
-//                      are summed through LDS at the end.
+//   bwd_kv_kernel      work item (sequence, KV head, 64 keys), 4 waves: wave w
+//                      holds K and V of 32 of the keys as MFMA fragments and
+//                      takes 4 of the 8 query heads; it walks every 32-query
+//                      block that can see its keys: S = Q K^T and dP = dO V^T
+//                      (8 + 8 MFMAs), P and dS in registers, then
+//                      dV^T += dO^T P and dK^T += Q^T dS (8 + 8 MFMAs; dO^T
+//                      and Q^T through a per-wave LDS tile and transpose
+//                      reads). The two waves of each 32 keys are summed
+//                      through LDS at the end.
 // dq, dk, dv are written once each (no atomics), rounded to bf16 from fp32.
 #include "common.h"
 #include "internal.h"
@@ -295,21 +296,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 }
 
 // ---------------------------------------------------------------------------
-// dk and dv: one work group of 4 waves per (sequence, KV head g, 64 keys). Wave
-// w takes the 32 keys t0 + 32 (w & 1) .. + 31 and query heads 8 g + 4 (w >> 1)
-// .. + 3, and holds fp32 dK^T and dV^T for its keys (64 VGPRs); the two waves of
-// a key half are summed through LDS at the end.
+// dk and dv: one work group of 4 waves per (sequence, KV head g, 128 keys).
+// Wave w holds K and V of the 32 keys t0 + 32 w .. + 31 as MFMA fragments and
+// fp32 dK^T, dV^T for them (64 VGPRs) over all 8 query heads of the group, so no
+// sum across waves is needed. The 4 waves walk the same steps (32 queries of
+// one head each) and share each step's q / dO rows through a double-buffered
+// LDS tile that each wave fills a quarter of: a row is fetched once per work
+// group, not once per wave.
 // ---------------------------------------------------------------------------
-constexpr int kKvLds = 4 * 2 * BQ * QS * 2;   // per-wave q and dO tiles (bytes); the final sum reuses them
-static_assert(4 * 8 * 64 * 16 <= kKvLds, "the cross-wave sum of one tensor fits in the tiles' space");
+constexpr int KT = kBackwardKT;   // keys per work group
+static_assert(KT == 4 * 32, "one wave per 32 keys");
 
 template <bool THD, bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[kKvLds];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_ld[4 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_t[2][2 * BQ * QS];   // [buffer][q tile, dO tile]
+  __shared__ __attribute__((aligned(16))) uint32_t lds_ld[2][2 * BQ];     // [buffer][(lse, D) per query]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int kh = wave & 1, hp = wave >> 1;
   const int Hkv = p.num_kv_heads;
   const int item = blockIdx.x / Hkv;
   const int g = blockIdx.x - item * Hkv;
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int n = min(max(w.x, 0), p.batch - 1);
     ts = min(max(__ldg(p.cu_seqlens + n), 0), p.seqlen);
     L = min(max(__ldg(p.cu_seqlens + n + 1), ts), p.seqlen) - ts;
-    jt = (L + NK - 1) / NK - 1 - w.y;   // the list counts tiles from the end: most queries first
+    jt = (L + KT - 1) / KT - 1 - w.y;   // the list counts tiles from the end: most queries first
     row0 = 0; bq_ = bk_ = bv_ = bd_ = 0;
   } else {
     const int r = item / p.batch, b = item - r * p.batch;
@@ -331,10 +334,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     row0 = (int64_t)b * p.seqlen;
     bq_ = b * p.q_sb; bk_ = b * p.k_sb; bv_ = b * p.v_sb; bd_ = b * p.do_sb;
   }
-  const int t0 = jt * NK;
-  if (jt < 0 || t0 >= L) return;
-  const int tlast = min(t0 + NK, L) - 1;
-  const int k0 = t0 + 32 * kh;   // the wave's first key
+  const int t0 = jt * KT;
+  if (jt < 0 || t0 >= L) return;   // uniform over the work group
+  const int tlast = min(t0 + KT, L) - 1;
+  const int k0 = t0 + 32 * wave;   // the wave's first key (past tlast: the wave only helps fetch)
   const int W = p.window;
   const uint32_t weff = (W > 0) ? (uint32_t)W : 0x7FFFFFFFu;
   const int qhi = (W > 0) ? min(L - 1, tlast + W - 1) : L - 1;   // last query that sees a key of the tile
@@ -358,76 +361,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int b = 0; b < 2; ++b) dkt[a][b] = dvt[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // the wave's q and dO tiles [32 queries][QS] for the transpose reads
-  bf16_t* lq = reinterpret_cast<bf16_t*>(lds_raw) + wave * (2 * BQ * QS);
-  bf16_t* ldo = lq + BQ * QS;
-  uint32_t* lld = lds_ld + wave * 64;
-
-  // Rows are read through buffer ranges that end with the sequence: rows past it
-  // read as zeros (their dO is 0, so they add nothing to dV or dK) and need no
-  // clamps; one 32-bit offset per load. Each fetch builds its head's ranges in
-  // scalar registers (the head is wave-uniform).
-  const int32_t qrow_b = (int32_t)p.q_st * 2, drow_b = (int32_t)p.do_st * 2;   // < 2^31 / (L + 32): host check
-  struct Fetch { uint4 qa[2][2], da[2][2]; uint32_t ld; };
-  auto fetch = [&](int qb, int hh, Fetch& f) __attribute__((always_inline)) {
+  // Fetch of a step's rows: wave w takes rows 8 w .. 8 w + 7 of the 32, lane =
+  // (row, 16-byte chunk). Rows are read through buffer ranges that end with the
+  // sequence: rows past it read as zeros (their dO is 0, so they add nothing to
+  // dV or dK) and need no clamps; one 32-bit offset per load (the host checks
+  // that a sequence's rows span less than 2 GiB). The (lse, D) words of the 32
+  // queries come with them, one per lane.
+  const int srow = 8 * wave + (lane >> 3), sch = lane & 7;
+  const int32_t qrow_b = (int32_t)p.q_st * 2, drow_b = (int32_t)p.do_st * 2;
+  uint4 sq, sd;
+  uint32_t sw;
+  auto fetch = [&](int qb, int hh) __attribute__((always_inline)) {
     const int q0 = qb * BQ;
-    const int head = g * kGroup + 4 * hp + hh;
+    const int head = g * kGroup + hh;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(p.q + bq_ + (int64_t)ts * p.q_st + (int64_t)head * p.q_sh, (L - 1) * qrow_b + 2 * kHeadDim);
     const __amdgpu_buffer_rsrc_t rd =
         make_rsrc(p.dout + bd_ + (int64_t)ts * p.do_st + (int64_t)head * p.do_sh, (L - 1) * drow_b + 2 * kHeadDim);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.ld + 2 * ((int64_t)head * p.tokens + row0 + ts), L * 8);
+    sq = ldb16(rq, (uint32_t)((q0 + srow) * qrow_b + 16 * sch));
+    sd = ldb16(rd, (uint32_t)((q0 + srow) * drow_b + 16 * sch));
+    sw = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)((2 * q0 + lane) * 4), 0, 0);
+  };
+  auto write_tile = [&](int buf) __attribute__((always_inline)) {
+    bf16_t* lq = lds_t[buf];
+    *reinterpret_cast<uint4*>(lq + srow * QS + 8 * sch) = sq;
+    *reinterpret_cast<uint4*>(lq + BQ * QS + srow * QS + 8 * sch) = sd;
+    if ((lane >> 4) == wave) lds_ld[buf][lane] = sw;   // words 16 w .. 16 w + 15
+  };
+
+  // One step: 32 queries (block qb) of head hh against the wave's 32 keys, from
+  // LDS buffer buf. A wave whose keys the block cannot see skips it.
+  auto step = [&](int buf, int qb) __attribute__((always_inline)) {
+    const int q0 = qb * BQ;
+    const bool none = (k0 > tlast) || (q0 + BQ - 1 < k0) || (W > 0 && q0 - (k0 + 31) >= W);
+    if (none) return;
+    const bool full = (q0 >= k0 + 31) && (W == 0 || q0 + BQ - 1 - k0 < W);
+    const bf16_t* lq = lds_t[buf];
+    const bf16_t* ldo = lq + BQ * QS;
+    const uint32_t* lld = lds_ld[buf];
+    // S = Q K^T and dP = dO V^T: [qm][kb] element e = query q0 + 16 qm + 4 grp + e,
+    // key k0 + 16 kb + col (q and dO rows as A operands: lane = query row, 8 dims)
+    f32x4_t s_[2][2], dp_[2][2];
 #pragma unroll
     for (int qm = 0; qm < 2; ++qm) {
-      // q~ and dO rows as A-operand fragments (lane = query row, 8 consecutive dims)
-      const uint32_t qo = (uint32_t)((q0 + qm * 16 + col) * qrow_b + 16 * grp);
-      const uint32_t dof = (uint32_t)((q0 + qm * 16 + col) * drow_b + 16 * grp);
-      f.qa[qm][0] = ldb16(rq, qo); f.qa[qm][1] = ldb16(rq, qo + 64);
-      f.da[qm][0] = ldb16(rd, dof); f.da[qm][1] = ldb16(rd, dof + 64);
-    }
-    // (lse, D) of the 32 queries: one float per lane, lane = 2 query + which
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.ld + 2 * ((int64_t)head * p.tokens + row0 + ts), L * 8);
-    f.ld = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)((2 * q0 + lane) * 4), 0, 0);
-  };
-  auto step = [&](int qb, int hh, const Fetch& f) __attribute__((always_inline)) {
-    const int q0 = qb * BQ;
-    const bool full = (q0 >= k0 + 31) && (W == 0 || q0 + BQ - 1 - k0 < W);
-    // the previous step's transpose reads are complete before the tiles are rewritten
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
+      const bf16_t* qr = lq + (qm * 16 + col) * QS + 8 * grp;
+      const bf16_t* dr = ldo + (qm * 16 + col) * QS + 8 * grp;
+      const bf16x8_t qa0 = as_bf16x8(*reinterpret_cast<const uint4*>(qr));
+      const bf16x8_t qa1 = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 32));
+      const bf16x8_t da0 = as_bf16x8(*reinterpret_cast<const uint4*>(dr));
+      const bf16x8_t da1 = as_bf16x8(*reinterpret_cast<const uint4*>(dr + 32));
 #pragma unroll
-    for (int qm = 0; qm < 2; ++qm)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        *reinterpret_cast<uint4*>(lq + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = f.qa[qm][ks];
-        *reinterpret_cast<uint4*>(ldo + (qm * 16 + col) * QS + 32 * ks + 8 * grp) = f.da[qm][ks];
+      for (int kb = 0; kb < 2; ++kb) {
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        s_[qm][kb] = mfma16(qa1, kf[kb][1], mfma16(qa0, kf[kb][0], z));
+        dp_[qm][kb] = mfma16(da1, vf[kb][1], mfma16(da0, vf[kb][0], z));
       }
-    lld[lane] = f.ld;
-    // Per 16-query half qm: S = Q K^T and dP = dO V^T ([kb] element e = query
-    // q0 + 16 qm + 4 grp + e, key k0 + 16 kb + col), then P and dS = P (dP - D),
-    // packed as B operands over the 32 queries (elements 4 qm .. 4 qm + 3)
+    }
+    // dO^T and Q^T as A operands (transpose reads of the row-major tiles)
+    bf16x8_t a_do[4], a_q[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int off = (4 * grp + (col >> 2)) * QS + 16 * db + 4 * (col & 3);
+      const uint2 dlo = lds_read_tr16(ldo + off), dhi = lds_read_tr16(ldo + off + 16 * QS);
+      const uint2 qlo = lds_read_tr16(lq + off), qhi2 = lds_read_tr16(lq + off + 16 * QS);
+      a_do[db] = __builtin_bit_cast(bf16x8_t, make_uint4(dlo.x, dlo.y, dhi.x, dhi.y));
+      a_q[db] = __builtin_bit_cast(bf16x8_t, make_uint4(qlo.x, qlo.y, qhi2.x, qhi2.y));
+    }
+    // P = exp(S - lse) and dS = P (dP - D), packed as B operands over the 32
+    // queries (elements 4 qm .. 4 qm + 3 of a lane's 8)
     uint32_t pw[2][4], dw[2][4];   // [kb][word]
 #pragma unroll
     for (int qm = 0; qm < 2; ++qm) {
-      // (lse, D) of the lane's queries q0 + 16 qm + 4 grp + e, e = 0..3 (a wave's LDS
-      // operations complete in order: the words written above are there)
       const uint4 x0 = *reinterpret_cast<const uint4*>(lld + 32 * qm + 8 * grp);
       const uint4 x1 = *reinterpret_cast<const uint4*>(lld + 32 * qm + 8 * grp + 4);
       const float l2[4] = {__uint_as_float(x0.x), __uint_as_float(x0.z), __uint_as_float(x1.x), __uint_as_float(x1.z)};
       const float dd[4] = {__uint_as_float(x0.y), __uint_as_float(x0.w), __uint_as_float(x1.y), __uint_as_float(x1.w)};
-      f32x4_t s_[2], dp_[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        s_[kb] = mfma16(as_bf16x8(f.qa[qm][1]), kf[kb][1], mfma16(as_bf16x8(f.qa[qm][0]), kf[kb][0], z));
-        dp_[kb] = mfma16(as_bf16x8(f.da[qm][1]), vf[kb][1], mfma16(as_bf16x8(f.da[qm][0]), vf[kb][0], z));
-      }
       if (!full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int qq = q0 + qm * 16 + 4 * grp + e, key = k0 + kb * 16 + col;
-            s_[kb][e] = ((uint32_t)(qq - key) < weff) ? s_[kb][e] : -INFINITY;
+            s_[qm][kb][e] = ((uint32_t)(qq - key) < weff) ? s_[qm][kb][e] : -INFINITY;
           }
       }
 #pragma unroll
@@ -435,8 +451,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         float pv[4], dv_[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[kb][e], sl, -l2[e]));
-          dv_[e] = pv[e] * (dp_[kb][e] - dd[e]);
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[qm][kb][e], sl, -l2[e]));
+          dv_[e] = pv[e] * (dp_[qm][kb][e] - dd[e]);
         }
         pw[kb][2 * qm] = pack_bf16x2(pv[0], pv[1]);
         pw[kb][2 * qm + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -444,77 +460,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         dw[kb][2 * qm + 1] = pack_bf16x2(dv_[2], dv_[3]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    // dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T read transposed from the tiles)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int off = (4 * grp + (col >> 2)) * QS + 16 * db + 4 * (col & 3);
-      const uint2 dlo = lds_read_tr16(ldo + off), dhi = lds_read_tr16(ldo + off + 16 * QS);
-      const uint2 qlo = lds_read_tr16(lq + off), qhi2 = lds_read_tr16(lq + off + 16 * QS);
-      const bf16x8_t a_do = __builtin_bit_cast(bf16x8_t, make_uint4(dlo.x, dlo.y, dhi.x, dhi.y));
-      const bf16x8_t a_q = __builtin_bit_cast(bf16x8_t, make_uint4(qlo.x, qlo.y, qhi2.x, qhi2.y));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        dvt[db][kb] = mfma16(a_do, __builtin_bit_cast(bf16x8_t, make_uint4(pw[kb][0], pw[kb][1], pw[kb][2], pw[kb][3])),
-                             dvt[db][kb]);
-        dkt[db][kb] = mfma16(a_q, __builtin_bit_cast(bf16x8_t, make_uint4(dw[kb][0], dw[kb][1], dw[kb][2], dw[kb][3])),
-                             dkt[db][kb]);
-      }
-    }
-  };
-
-  // Steps: every block of 32 queries that can see the tile, walked from the last
-  // one down, once per head of the wave. The work groups of one (sequence, KV
-  // head) run together on one XCD (consecutive work groups take consecutive KV
-  // heads, dealt round-robin over the 8 XCDs) and then read the same q / dO
-  // block at about the same time, so L2 serves the repeats. Two buffers of q /
-  // dO rows (and their lse and D) take turns: a step computes from one while
-  // the other receives the next step's rows (no register copies between steps).
-  const int qb_lo = t0 / BQ, qb_hi = qhi / BQ;
-  Fetch fa, fb;
-  fetch(qb_hi, 0, fa);
-  for (int qb = qb_hi; qb >= qb_lo; --qb) {
-    fetch(qb, 1, fb);
-    step(qb, 0, fa);
-    fetch(qb, 2, fa);
-    step(qb, 1, fb);
-    fetch(qb, 3, fb);
-    step(qb, 2, fa);
-    fetch(max(qb - 1, qb_lo), 0, fa);   // the last block fetches itself again: no branch
-    step(qb, 3, fb);
-  }
-
-  // sum the two waves of each key half through LDS (waves kh and kh + 2); wave w
-  // finishes d blocks (w >> 1, (w >> 1) + 2) -- the rotation pairs dims i and
-  // i + 32 -- of the key half w & 1
-  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds_raw);
-  const int pr = wave >> 1;
-#pragma unroll 1
-  for (int which = 0; which < 2; ++which) {
-    __syncthreads();
+    // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) red[(wave * 8 + db * 2 + kb) * 64 + lane] = which ? dvt[db][kb] : dkt[db][kb];
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = k0 + kb * 16 + col;
-      f32x4_t y1 = red[(kh * 8 + pr * 2 + kb) * 64 + lane] + red[((kh + 2) * 8 + pr * 2 + kb) * 64 + lane];
-      f32x4_t y2 = red[(kh * 8 + (pr + 2) * 2 + kb) * 64 + lane] + red[((kh + 2) * 8 + (pr + 2) * 2 + kb) * 64 + lane];
-      if (key > tlast) continue;
-      if (which == 0) {
-        y1 *= p.scale;
-        y2 *= p.scale;
-        if (ROT) {
-          const bf16_t* tp = p.table + (int64_t)min(key, p.table_rows - 1) * kHeadDim + 16 * pr + 4 * grp;
-          rotate_back4(y1, y2, ldg8(tp), ldg8(tp + 32));
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        dvt[db][kb] = mfma16(a_do[db], __builtin_bit_cast(bf16x8_t, make_uint4(pw[kb][0], pw[kb][1], pw[kb][2], pw[kb][3])),
+                             dvt[db][kb]);
+        dkt[db][kb] = mfma16(a_q[db], __builtin_bit_cast(bf16x8_t, make_uint4(dw[kb][0], dw[kb][1], dw[kb][2], dw[kb][3])),
+                             dkt[db][kb]);
       }
-      bf16_t* op = (which ? p.dv : p.dk) + ((row0 + ts + key) * Hkv + g) * kHeadDim + 16 * pr + 4 * grp;
-      *reinterpret_cast<uint2*>(op) = pack4(y1);
-      *reinterpret_cast<uint2*>(op + 32) = pack4(y2);
+  };
+
+  // Steps: every block of 32 queries that can see the tile, walked from the last
+  // one down, each for the 8 query heads. The work groups of one (sequence, KV
+  // head) run together on one XCD (consecutive work groups take consecutive KV
+  // heads, dealt round-robin over the 8 XCDs) and then read the same q / dO
+  // block at about the same time, so L2 serves the repeats. A step's rows are
+  // fetched during the step before and written to the other LDS buffer at its
+  // end; one barrier per step. The last step fetches its own rows again (no
+  // branch around the loads).
+  const int qb_lo = t0 / BQ, qb_hi = qhi / BQ;
+  const int nsteps = (qb_hi - qb_lo + 1) * kGroup;
+  fetch(qb_hi, 0);
+  write_tile(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int n = min(s + 1, nsteps - 1);
+    fetch(qb_hi - n / kGroup, n % kGroup);
+    step(s & 1, qb_hi - s / kGroup);
+    write_tile((s & 1) ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: dk~ = tau dK^T, dk = R^T dk~ (the rotation pairs dims i and i + 32:
+  // d blocks pr and pr + 2 of the same lane); dv as accumulated
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = k0 + kb * 16 + col;
+    if (key > tlast) continue;
+    const int64_t orow = ((row0 + ts + key) * Hkv + g) * kHeadDim + 4 * grp;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      f32x4_t y1 = dkt[pr][kb] * p.scale, y2 = dkt[pr + 2][kb] * p.scale;
+      if (ROT) {
+        const bf16_t* tp = p.table + (int64_t)min(key, p.table_rows - 1) * kHeadDim + 16 * pr + 4 * grp;
+        rotate_back4(y1, y2, ldg8(tp), ldg8(tp + 32));
+      }
+      *reinterpret_cast<uint2*>(p.dk + orow + 16 * pr) = pack4(y1);
+      *reinterpret_cast<uint2*>(p.dk + orow + 16 * pr + 32) = pack4(y2);
+      *reinterpret_cast<uint2*>(p.dv + orow + 16 * pr) = pack4(dvt[pr][kb]);
+      *reinterpret_cast<uint2*>(p.dv + orow + 16 * pr + 32) = pack4(dvt[pr + 2][kb]);
     }
   }
 }

@@ -91,7 +91,8 @@ struct BackwardParams {
 hipError_t launch_backward(const BackwardParams& p, bool thd, hipStream_t stream);
 // x[0 .. n) = value (a kernel, not a memset: safe inside captured graphs)
 hipError_t launch_fill_f32(float* x, int32_t n, float value, hipStream_t stream);
-constexpr int kBackwardNK = 64;  // keys per tile of the backward kernels
+constexpr int kBackwardNK = 64;   // keys per K / V tile of the backward dq kernel
+constexpr int kBackwardKT = 128;  // keys per work item of the backward dk / dv kernel
 
 // ---- decode ----
 struct DecodeParams {

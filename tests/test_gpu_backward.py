@@ -1,7 +1,7 @@
 """GPU parity of the prefill backward (dq, dk, dv, dsinks) and the forward's
 log-sum-exp against the fp64 oracle (oracle.backward), through the C ABI.
 
-Sizes span several 64-key tiles and 32-query blocks with ragged tails, full
+Sizes span several 128-key work items and 32-query blocks with ragged tails, full
 causal and window layers, BSHD and packed THD, one and two KV heads. The
 gradient tolerance is stated in the design doc and written in grad_close below.
 """
@@ -171,7 +171,7 @@ def test_backward_special_sinks(table):
 @pytest.mark.parametrize("window", [0, 128])
 def test_backward_full_size_sampled(table, window):
     """The benchmark's configuration (dense B=4 S=4096, both layers, the same inputs and
-    dO as bench.py): dq on 32 sampled query rows and dk, dv on whole 64-key tiles,
+    dO as bench.py): dq on 32 sampled query rows and dk, dv on whole 128-key work items,
     of batch 3, against the oracle's exact gradients at those rows and keys."""
     inp = wl.dense()
     dout = wl.grad_out(inp.q.shape, 7)
@@ -185,7 +185,7 @@ def test_backward_full_size_sampled(table, window):
     extra = torch.randperm(4096, generator=torch.Generator().manual_seed(17))[:24].tolist()
     rows = sorted(set([0, 1, 31, 32, 63, 64, 2047, 4095] + extra))
     f64 = lambda t: t[b].double().numpy()
-    tiles = [(4032, 4096)] + ([(2048, 2112), (0, 64)] if window else [])
+    tiles = [(3968, 4096)] + ([(2048, 2176), (0, 128)] if window else [])
     for lo, hi in tiles:
         ref = oracle.prefill_backward_rows(f64(inp.q), f64(inp.k), f64(inp.v), np64(inp.sinks), TAU, window,
                                            f64(dout), rows, lo, hi, CFG)
