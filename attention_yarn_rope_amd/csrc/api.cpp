@@ -366,7 +366,7 @@ size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc) 
              round_up((size_t)thd_items(desc, kBackwardKT) * sizeof(int2)) + kAlign;
   bytes += round_up(T * hq * kHeadDim * sizeof(uint16_t));    // rotated q
   bytes += round_up(T * hkv * kHeadDim * sizeof(uint16_t));   // rotated k
-  bytes += round_up(T * hq * 2 * sizeof(float));              // (lse in log2 units, D = <dO, o>), head-major
+  bytes += round_up(T * hq * 2 * sizeof(float));              // (lse in log2 units, -<dO, o>), head-major
   return bytes;
 }
 

@@ -20,7 +20,8 @@
 //                      accumulates dQ^T += K^T dS^T (16 MFMAs, K^T read from
 //                      the row-major K tile with ds_read_b64_tr_b16). It also
 //                      forms D = <dO, o> per row and writes (lse in log2
-//                      units, D) head-major for the kernels after it.
+//                      units, -D) head-major for the kernels after it; the
+//                      dP sums start from -D, so dP - D needs no subtraction.
 //   bwd_sink_kernel    dsigma per head: one work group per head sums its rows
 //                      in a fixed order (no atomics, reproducible).
 //   bwd_kv_kernel      work item (sequence, KV head, 64 keys), 4 waves: wave w
@@ -49,7 +50,7 @@ __device__ __forceinline__ uint2 ldg8(const bf16_t* p) { return *reinterpret_cas
 
 // dsigma_h = - sum over the head's rows of exp(sigma_h - lse) * D, one work
 // group per head, each thread summing a fixed stride of rows, then a tree.
-// D and lse (log2 units) come head-major from the dq kernel; packed tokens
+// lse (log2 units) and -D come head-major from the dq kernel; packed tokens
 // after the last sequence belong to none and are left out.
 template <bool THD>
 __global__ __launch_bounds__(256) void bwd_sink_kernel(BackwardParams p) {
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(BackwardParams p) {
   if (sig2 > -INFINITY) {
     for (int64_t t = threadIdx.x; t < rows; t += 256) {
       const float2 x = ld[t];
-      acc -= __builtin_amdgcn_exp2f(sig2 - x.x) * x.y;
+      acc += __builtin_amdgcn_exp2f(sig2 - x.x) * x.y;   // x.y = -D
     }
   }
   part[threadIdx.x] = acc;
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   // after this kernel.
   int qpos[2];
   bf16x8_t qf[2][2], df[2][2];
-  float lse2[2], dd[2];
+  float lse2[2];
+  f32x4_t negd[2];   // -D of the lane's query, the starting value of the dP^T sums
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     qpos[cb] = q0 + 16 * cb + col;
@@ -187,10 +189,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
              bf16_lo(pd1[i]) * bf16_lo(po1[i]) + bf16_hi(pd1[i]) * bf16_hi(po1[i]);
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
-    dd[cb] = dot;
+    negd[cb] = f32x4_t{-dot, -dot, -dot, -dot};
     if (grp == 0 && qpos[cb] <= qlast) {
       const int64_t rr = (int64_t)head * p.tokens + row0 + ts + pos;
-      reinterpret_cast<float2*>(p.ld)[rr] = make_float2(lse2[cb], dot);
+      reinterpret_cast<float2*>(p.ld)[rr] = make_float2(lse2[cb], -dot);
     }
   }
 
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     const bf16_t* vt = lds_v + buf * NK * VSB;
     const int tile0 = kv_lo + t * NK;
 
-    // S^T = K Q^T and dP^T = V dO^T: [kb][cb] element r = key kb*16 + 4*grp + r, query col
+    // S^T = K Q^T and dP^T - D = V dO^T - D: [kb][cb] element r = key kb*16 + 4*grp + r, query col
     f32x4_t s[4][2], dpt[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int cb = 0; cb < 2; ++cb) {
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         s[kb][cb] = mfma16(a1, qf[cb][1], mfma16(a0, qf[cb][0], z));
-        dpt[kb][cb] = mfma16(c1, df[cb][1], mfma16(c0, df[cb][0], z));
+        dpt[kb][cb] = mfma16(c1, df[cb][1], mfma16(c0, df[cb][0], negd[cb]));   // dP^T - D
       }
     }
     const bool full = (tile0 + NK - 1 <= q0) && (W == 0 || qlast - tile0 < W);
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][cb][r], sl, -lse2[cb]));
-          x[r] = pr * (dpt[kb][cb][r] - dd[cb]);
+          x[r] = pr * dpt[kb][cb][r];
         }
         w[2 * kb] = pack_bf16x2(x[0], x[1]);
         w[2 * kb + 1] = pack_bf16x2(x[2], x[3]);
@@ -310,7 +312,7 @@ static_assert(KT == 4 * 32, "one wave per 32 keys");
 template <bool THD, bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_t[2][2 * BQ * QS];   // [buffer][q tile, dO tile]
-  __shared__ __attribute__((aligned(16))) uint32_t lds_ld[2][2 * BQ];     // [buffer][(lse, D) per query]
+  __shared__ __attribute__((aligned(16))) float lds_ld[2][2 * BQ];        // [buffer][lse of 32 queries, -D of 32]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int Hkv = p.num_kv_heads;
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // (row, 16-byte chunk). Rows are read through buffer ranges that end with the
   // sequence: rows past it read as zeros (their dO is 0, so they add nothing to
   // dV or dK) and need no clamps; one 32-bit offset per load (the host checks
-  // that a sequence's rows span less than 2 GiB). The (lse, D) words of the 32
+  // that a sequence's rows span less than 2 GiB). The (lse, -D) words of the 32
   // queries come with them, one per lane.
   const int srow = 8 * wave + (lane >> 3), sch = lane & 7;
   const int32_t qrow_b = (int32_t)p.q_st * 2, drow_b = (int32_t)p.do_st * 2;
@@ -387,7 +389,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     bf16_t* lq = lds_t[buf];
     *reinterpret_cast<uint4*>(lq + srow * QS + 8 * sch) = sq;
     *reinterpret_cast<uint4*>(lq + BQ * QS + srow * QS + 8 * sch) = sd;
-    if ((lane >> 4) == wave) lds_ld[buf][lane] = sw;   // words 16 w .. 16 w + 15
+    // words 16 w .. 16 w + 15 of the 64, split into the lse and -D vectors
+    if ((lane >> 4) == wave) lds_ld[buf][(lane & 1) * BQ + (lane >> 1)] = __uint_as_float(sw);
   };
 
   // One step: 32 queries (block qb) of head hh against the wave's 32 keys, from
@@ -399,8 +402,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const bool full = (q0 >= k0 + 31) && (W == 0 || q0 + BQ - 1 - k0 < W);
     const bf16_t* lq = lds_t[buf];
     const bf16_t* ldo = lq + BQ * QS;
-    const uint32_t* lld = lds_ld[buf];
-    // S = Q K^T and dP = dO V^T: [qm][kb] element e = query q0 + 16 qm + 4 grp + e,
+    const float* lld = lds_ld[buf];
+    // lse (log2 units) and -D of the lane's queries q0 + 16 qm + 4 grp + e, e = 0..3
+    f32x4_t l2[2], negd[2];
+#pragma unroll
+    for (int qm = 0; qm < 2; ++qm) {
+      l2[qm] = *reinterpret_cast<const f32x4_t*>(lld + 16 * qm + 4 * grp);
+      negd[qm] = *reinterpret_cast<const f32x4_t*>(lld + BQ + 16 * qm + 4 * grp);
+    }
+    // S = Q K^T and dP - D = dO V^T - D: [qm][kb] element e = query q0 + 16 qm + 4 grp + e,
     // key k0 + 16 kb + col (q and dO rows as A operands: lane = query row, 8 dims)
     f32x4_t s_[2][2], dp_[2][2];
 #pragma unroll
@@ -415,7 +425,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int kb = 0; kb < 2; ++kb) {
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         s_[qm][kb] = mfma16(qa1, kf[kb][1], mfma16(qa0, kf[kb][0], z));
-        dp_[qm][kb] = mfma16(da1, vf[kb][1], mfma16(da0, vf[kb][0], z));
+        dp_[qm][kb] = mfma16(da1, vf[kb][1], mfma16(da0, vf[kb][0], negd[qm]));
       }
     }
     // dO^T and Q^T as A operands (transpose reads of the row-major tiles)
@@ -433,10 +443,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     uint32_t pw[2][4], dw[2][4];   // [kb][word]
 #pragma unroll
     for (int qm = 0; qm < 2; ++qm) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(lld + 32 * qm + 8 * grp);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(lld + 32 * qm + 8 * grp + 4);
-      const float l2[4] = {__uint_as_float(x0.x), __uint_as_float(x0.z), __uint_as_float(x1.x), __uint_as_float(x1.z)};
-      const float dd[4] = {__uint_as_float(x0.y), __uint_as_float(x0.w), __uint_as_float(x1.y), __uint_as_float(x1.w)};
       if (!full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -451,8 +457,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         float pv[4], dv_[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[qm][kb][e], sl, -l2[e]));
-          dv_[e] = pv[e] * (dp_[qm][kb][e] - dd[e]);
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[qm][kb][e], sl, -l2[qm][e]));
+          dv_[e] = pv[e] * dp_[qm][kb][e];
         }
         pw[kb][2 * qm] = pack_bf16x2(pv[0], pv[1]);
         pw[kb][2 * qm + 1] = pack_bf16x2(pv[2], pv[3]);

@@ -69,7 +69,7 @@ struct BackwardParams {
   const uint16_t* dout; int64_t do_sb, do_st, do_sh;
   const float* lse;              // [tokens, Hq] natural log, from the forward
   float* ld;                     // workspace [Hq, tokens, 2]: per row lse in log2 units (+inf for a row
-                                 // without any term) and D = <dO, o>
+                                 // without any term) and -D = -<dO, o>
   int64_t tokens;                // rows of the token-major tensors (BSHD batch * seqlen, THD seqlen)
   const float* sinks;
   float* dsinks;                 // [Hq]
