@@ -26,6 +26,10 @@ Sources (the pages are cited by title and section):
   * "gpt-oss-20b 模型结构" (model-structure print-out): q_proj 2880->4096,
     k_proj / v_proj 2880->512, so 64 query heads and 8 KV heads of width 64.
 
+``oracle.kvcache`` keeps the keys and values of the decode loop in contiguous,
+paged and ring caches (append, and decode over a cache); no page specifies a
+cache, so its layouts are readings, pinned against the prefill definition.
+
 ``oracle.backward`` adds the log-sum-exp of each row and the gradients of the
 attention with respect to q, k, v and the sinks: the derivatives of the same
 definition (no page prints a backward pass).
@@ -46,6 +50,7 @@ from .attention import (
     prefill_rows,
     decode,
 )
+from . import kvcache
 from .backward import (rotate_transpose, sink_attention_backward, prefill_bshd_backward, prefill_thd_backward,
                        prefill_backward_rows)
 
@@ -55,5 +60,5 @@ __all__ = [
     "rotate", "rope_qk_bshd", "rope_qk_thd", "thd_positions",
     "sink_attention", "prefill_bshd", "prefill_thd", "prefill_rows", "decode",
     "rotate_transpose", "sink_attention_backward", "prefill_bshd_backward", "prefill_thd_backward",
-    "prefill_backward_rows",
+    "prefill_backward_rows", "kvcache",
 ]
