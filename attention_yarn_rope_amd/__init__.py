@@ -1,5 +1,6 @@
 """GPT-OSS attention hot path on MI355X: YaRN RoPE, sink + GQA + sliding-window
-prefill (BSHD and packed THD) with its backward pass, and split-KV decode, as
+prefill (BSHD and packed THD) with its backward pass, split-KV decode over
+contiguous, paged or ring KV caches and the cache append, as
 hand-written gfx950 HIP kernels behind a C ABI (include/gptoss_attn.h). This
 package is the thin torch binding; libgptoss_attn.so is loaded on first use and
 is required.
@@ -14,6 +15,10 @@ from .api import (  # noqa: F401
     attn_prefill_lse,
     attn_prefill_backward,
     attn_decode,
+    kv_layout,
+    kv_append,
+    attn_decode_kv,
+    decode_kv_workspace_size,
     prefill_workspace_size,
     prefill_backward_workspace_size,
     decode_workspace_size,

@@ -30,6 +30,13 @@ class SeqDesc(ctypes.Structure):
                 ("cu_seqlens", c_vp), ("num_q_heads", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32)]
 
 
+class KVLayout(ctypes.Structure):
+    _fields_ = [("kind", c_i32), ("capacity", c_i32), ("strides", I64x3), ("block_table", c_vp),
+                ("max_pages", c_i32), ("num_pages", c_i32)]
+
+
+CACHE_KINDS = {"contiguous": 0, "paged": 1, "ring": 2}
+
 # name -> (restype, argtypes); every symbol include/gptoss_attn.h declares
 SIGNATURES = {
     "gptoss_abi_version": (ctypes.c_int, []),
@@ -56,6 +63,12 @@ SIGNATURES = {
                                                     c_vp, I64x3, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                     c_vp, c_size, c_vp]),
     "gptoss_attn_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "gptoss_kv_append": (ctypes.c_int, [ctypes.POINTER(KVLayout), c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, I64x3,
+                                        c_vp, I64x3, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp]),
+    "gptoss_attn_decode_kv_workspace_size": (c_size, [ctypes.POINTER(KVLayout), c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "gptoss_attn_decode_kv": (ctypes.c_int, [ctypes.POINTER(KVLayout), c_i32, c_i32, c_i32, c_i32, c_vp, I64x2,
+                                             c_vp, c_vp, c_vp, c_i32, c_vp, c_f32, c_i32, c_vp, c_i32, c_i32,
+                                             c_vp, I64x2, c_vp, c_size, c_i32, c_vp]),
     "gptoss_attn_decode": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, I64x2, c_vp, c_vp, I64x3,
                                           c_vp, c_i32, c_vp, c_f32, c_i32, c_vp, c_i32, c_i32, c_vp, I64x2,
                                           c_vp, c_size, c_i32, c_vp]),

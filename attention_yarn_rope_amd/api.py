@@ -10,7 +10,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import RopeConfig, SeqDesc, I64x2, I64x3, check
+from ._lib import RopeConfig, SeqDesc, KVLayout, I64x2, I64x3, check
 
 HEAD_DIM = 64
 
@@ -231,4 +231,100 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, sinks, window=0, table=None,
         I64x3(ks[0], ks[1], ks[2]), _ptr(cache_seqlens), Lmax, _ptr(sinks), float(scale), int(window),
         tptr, trows, tdim, _ptr(out), I64x2(out.stride(0), out.stride(1)), _ptr(workspace),
         workspace.numel(), int(num_splits), _stream()))
+    return out
+
+
+def kv_layout(k_cache, kind="contiguous", block_table=None):
+    """The gptoss_kv_layout of a cache tensor. Contiguous and ring caches are
+    [N, capacity, Hkv, D]; a paged pool is [num_pages, page_size, Hkv, D] with a
+    device int32 block_table [N, max_pages]."""
+    if kind not in _lib.CACHE_KINDS:
+        raise ValueError(f"kind must be one of {sorted(_lib.CACHE_KINDS)}")
+    if k_cache.dim() != 4:
+        raise ValueError("a cache is a 4-d tensor")
+    s = k_cache.stride()
+    lay = KVLayout()
+    lay.kind = _lib.CACHE_KINDS[kind]
+    lay.capacity = k_cache.shape[1]
+    lay.strides = I64x3(s[0], s[1], s[2])
+    if kind == "paged":
+        if block_table is None or block_table.dtype != torch.int32 or not block_table.is_cuda or \
+                block_table.dim() != 2 or not block_table.is_contiguous():
+            raise TypeError("a paged cache needs a contiguous CUDA int32 block_table [N, max_pages]")
+        lay.block_table = block_table.data_ptr()
+        lay.max_pages = block_table.shape[1]
+        lay.num_pages = k_cache.shape[0]
+    return lay
+
+
+def _cache_max_seqlen(kind, k_cache, block_table, table):
+    if kind == "contiguous":
+        return k_cache.shape[1]
+    if kind == "paged":
+        return block_table.shape[1] * k_cache.shape[1]
+    return table.shape[0] if table is not None else 2 ** 30
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, cache_seqlens, kind="contiguous", block_table=None, table=None,
+              max_seqlen=None):
+    """Store the newest tokens of every sequence: k_new / v_new [N, T, Hkv, D] (or [N, Hkv, D] for
+    one token) at positions cache_seqlens - T .. cache_seqlens - 1, k rotated there with the table."""
+    _bf16(k_cache, "k_cache"), _bf16(v_cache, "v_cache"), _bf16(k_new, "k_new"), _bf16(v_new, "v_new")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_new.dim() == 3:
+        k_new, v_new = k_new.unsqueeze(1), v_new.unsqueeze(1)
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have one shape")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda:
+        raise TypeError("cache_seqlens must be a CUDA int32 tensor")
+    N, T, Hkv, D = k_new.shape
+    lay = kv_layout(k_cache, kind, block_table)
+    if max_seqlen is None:
+        max_seqlen = _cache_max_seqlen(kind, k_cache, block_table, table)
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    kn, vn = k_new.stride(), v_new.stride()
+    check("gptoss_kv_append", _lib.load().gptoss_kv_append(
+        ctypes.byref(lay), _ptr(k_cache), _ptr(v_cache), N, Hkv, D, T, _ptr(k_new), I64x3(kn[0], kn[1], kn[2]),
+        _ptr(v_new), I64x3(vn[0], vn[1], vn[2]), _ptr(cache_seqlens), int(max_seqlen), tptr, trows, tdim, _stream()))
+
+
+def decode_kv_workspace_size(q, k_cache, kind="contiguous", block_table=None, window=0, max_seqlen=None,
+                             table=None, num_splits=0):
+    lay = kv_layout(k_cache, kind, block_table)
+    if max_seqlen is None:
+        max_seqlen = _cache_max_seqlen(kind, k_cache, block_table, table)
+    return _lib.load().gptoss_attn_decode_kv_workspace_size(ctypes.byref(lay), q.shape[0], q.shape[1],
+                                                             int(max_seqlen), int(window), int(num_splits))
+
+
+def attn_decode_kv(q, k_cache, v_cache, cache_seqlens, sinks, kind="contiguous", block_table=None, window=0,
+                   table=None, max_seqlen=None, softmax_scale=None, num_splits=0, out=None, workspace=None):
+    """attn_decode over a contiguous, paged or ring cache (kind); a ring needs window == its slot count."""
+    _bf16(q, "q"), _bf16(k_cache, "k_cache"), _bf16(v_cache, "v_cache")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda:
+        raise TypeError("cache_seqlens must be a CUDA int32 tensor")
+    if sinks.dtype != torch.float32 or not sinks.is_cuda or not sinks.is_contiguous():
+        raise TypeError("sinks must be a contiguous CUDA float32 tensor")
+    N, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    lay = kv_layout(k_cache, kind, block_table)
+    if max_seqlen is None:
+        max_seqlen = _cache_max_seqlen(kind, k_cache, block_table, table)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lib = _lib.load()
+    need = lib.gptoss_attn_decode_kv_workspace_size(ctypes.byref(lay), N, Hq, int(max_seqlen), int(window),
+                                                    int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    check("gptoss_attn_decode_kv", lib.gptoss_attn_decode_kv(
+        ctypes.byref(lay), N, Hq, Hkv, D, _ptr(q), I64x2(q.stride(0), q.stride(1)), _ptr(k_cache), _ptr(v_cache),
+        _ptr(cache_seqlens), int(max_seqlen), _ptr(sinks), float(scale), int(window), tptr, trows, tdim,
+        _ptr(out), I64x2(out.stride(0), out.stride(1)), _ptr(workspace), workspace.numel(), int(num_splits),
+        _stream()))
     return out

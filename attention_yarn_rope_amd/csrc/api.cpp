@@ -500,59 +500,52 @@ static int32_t decode_slots() {
   return 2 * cus;
 }
 
-size_t gptoss_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_cache_len,
-                                         int32_t num_splits) {
-  if (num_seqs < 0 || num_q_heads < 0 || max_cache_len < 1 || num_splits < 0) return 0;
-  const int64_t cap = decode_split_cap(max_cache_len, num_splits);
+static size_t decode_ws_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_keys, int32_t num_splits) {
+  const int64_t cap = decode_split_cap(max_keys, num_splits);
   const size_t slots = (size_t)num_seqs * num_q_heads * cap;
   // partials, then the split plan: 2 ints + one int2 per (sequence, split) item
   return round_up(slots * kHeadDim * sizeof(float)) + round_up(slots * 2 * sizeof(float)) +
          round_up(2 * sizeof(int32_t) + (size_t)num_seqs * cap * 2 * sizeof(int32_t));
 }
 
-gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 const void* q, const int64_t q_strides[2], const void* k_cache,
-                                 const void* v_cache, const int64_t kv_strides[3],
-                                 const int32_t* cache_seqlens, int32_t max_cache_len, const float* sinks,
-                                 float softmax_scale, int32_t window, const void* table, int32_t table_rows,
-                                 int32_t rotary_dim, void* out, const int64_t o_strides[2], void* workspace,
-                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
+size_t gptoss_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_cache_len,
+                                         int32_t num_splits) {
+  if (num_seqs < 0 || num_q_heads < 0 || max_cache_len < 1 || num_splits < 0) return 0;
+  return decode_ws_bytes(num_seqs, num_q_heads, max_cache_len, num_splits);
+}
+
+// Checks shared by both decode entry points; p gets q, sinks, table, out.
+static gptoss_status decode_args(DecodeParams& p, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, const void* q, const int64_t q_strides[2], const void* k_cache,
+                                 const void* v_cache, const int32_t* cache_seqlens, int32_t max_len,
+                                 const float* sinks, float softmax_scale, int32_t window, const void* table,
+                                 int32_t table_rows, int32_t rotary_dim, void* out, const int64_t o_strides[2],
+                                 int32_t num_splits) {
   if (num_seqs < 0) return fail(GPTOSS_ERR_SHAPE, "num_seqs must be >= 0");
   if (head_dim != kHeadDim) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", head_dim);
   if (num_kv_heads < 1 || num_q_heads != kGroup * num_kv_heads)
     return fail(GPTOSS_ERR_UNSUPPORTED, "num_q_heads %d must be 8 x num_kv_heads %d", num_q_heads, num_kv_heads);
-  if (max_cache_len < 1) return fail(GPTOSS_ERR_SHAPE, "max_cache_len must be >= 1");
+  if (max_len < 1) return fail(GPTOSS_ERR_SHAPE, "the maximum cache length must be >= 1");
   if (num_splits < 0) return fail(GPTOSS_ERR_SHAPE, "num_splits must be >= 0");
   if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
     return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (num_seqs == 0) return GPTOSS_OK;
-  if (!q || !k_cache || !v_cache || !cache_seqlens || !sinks || !out || !q_strides || !kv_strides || !o_strides)
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !sinks || !out || !q_strides || !o_strides)
     return fail(GPTOSS_ERR_NULL, "q, caches, cache_seqlens, sinks, out and all strides are required");
-  if (!strides_ok(q_strides, 2) || !strides_ok(kv_strides, 3) || !aligned16(q) || !aligned16(k_cache) ||
-      !aligned16(v_cache))
+  if (!strides_ok(q_strides, 2) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
   if (o_strides[0] < 0 || o_strides[1] < 0 || (o_strides[0] & 1) || (o_strides[1] & 1) ||
       (reinterpret_cast<uintptr_t>(out) & 3))
     return fail(GPTOSS_ERR_UNSUPPORTED, "out must be 4-byte aligned with even strides");
-  if (kv_strides[1] < kHeadDim || (int64_t)max_cache_len * kv_strides[1] * 2 > (int64_t)INT32_MAX)
-    return fail(GPTOSS_ERR_UNSUPPORTED,
-                "kv_strides[1] must be >= 64 and one sequence's rows must span less than 2 GiB");
-  gptoss_status st = check_table(table, table_rows, rotary_dim, max_cache_len);
+  gptoss_status st = check_table(table, table_rows, rotary_dim, max_len);
   if (st != GPTOSS_OK) return st;
-  const size_t need = gptoss_attn_decode_workspace_size(num_seqs, num_q_heads, max_cache_len, num_splits);
-  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
-    return fail(GPTOSS_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                workspace_bytes);
-  DecodeParams p;
-  memset(&p, 0, sizeof p);
   p.q = static_cast<const uint16_t*>(q);
   p.q_sn = q_strides[0]; p.q_sh = q_strides[1];
   p.k = static_cast<const uint16_t*>(k_cache);
   p.v = static_cast<const uint16_t*>(v_cache);
-  p.kv_sn = kv_strides[0]; p.kv_sp = kv_strides[1]; p.kv_sh = kv_strides[2];
   p.cache_seqlens = cache_seqlens;
-  p.max_cache_len = max_cache_len;
+  p.max_cache_len = max_len;
   p.num_seqs = num_seqs;
   p.num_kv_heads = num_kv_heads;
   p.window = window;
@@ -560,8 +553,19 @@ gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t 
   p.sinks = sinks;
   p.table = static_cast<const uint16_t*>(table);
   p.table_rows = table_rows;
-  // window layers only ever read the last `window` rows: fewer splits
-  const int32_t eff = (window > 0 && window < max_cache_len) ? window : max_cache_len;
+  p.o = static_cast<uint16_t*>(out);
+  p.o_sn = o_strides[0]; p.o_sh = o_strides[1];
+  return GPTOSS_OK;
+}
+
+// Split sizing, workspace carving and launch. eff: most keys one sequence reads
+// (the workspace was sized for ws_keys >= eff).
+static gptoss_status decode_run(DecodeParams& p, int32_t num_q_heads, int32_t eff, int32_t ws_keys,
+                                void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
+  const size_t need = decode_ws_bytes(p.num_seqs, num_q_heads, ws_keys, num_splits);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return fail(GPTOSS_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
   if (num_splits == 1 || (num_splits == 0 && eff <= kDecodeMinChunk)) {
     // one split per sequence (e.g. window layers): no plan, work item = sequence
     p.direct_chunk = (eff + 127) / 128 * 128;
@@ -575,19 +579,165 @@ gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t 
     p.target_chunks = decode_slots() * 13 / 10;
     p.num_splits = (eff + kDecodeMinChunk - 1) / kDecodeMinChunk;
   }
-  // p.num_splits <= decode_split_cap(): the partial buffers fit the workspace
+  // p.num_splits <= decode_split_cap(ws_keys): the partial buffers fit the workspace
   char* ws = static_cast<char*>(workspace);
-  const size_t cap = (size_t)num_seqs * num_q_heads * decode_split_cap(max_cache_len, num_splits);
+  const size_t cap = (size_t)p.num_seqs * num_q_heads * decode_split_cap(ws_keys, num_splits);
   p.part_o = reinterpret_cast<float*>(ws);
   p.part_ml = reinterpret_cast<float*>(ws + round_up(cap * kHeadDim * sizeof(float)));
   p.plan = reinterpret_cast<int32_t*>(ws + round_up(cap * kHeadDim * sizeof(float)) + round_up(cap * 2 * sizeof(float)));
   // work groups: enough for every item of the largest plan, at most two per slot (they loop)
-  const int64_t max_items = (int64_t)num_seqs * p.num_splits;
+  const int64_t max_items = (int64_t)p.num_seqs * p.num_splits;
   const int64_t groups = (int64_t)decode_slots() * 2;
   p.max_items = (int32_t)(max_items < groups ? max_items : groups);
-  p.o = static_cast<uint16_t*>(out);
-  p.o_sn = o_strides[0]; p.o_sh = o_strides[1];
   return hip_status(launch_decode(p, static_cast<hipStream_t>(stream)), "decode kernels");
+}
+
+gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 const void* q, const int64_t q_strides[2], const void* k_cache,
+                                 const void* v_cache, const int64_t kv_strides[3],
+                                 const int32_t* cache_seqlens, int32_t max_cache_len, const float* sinks,
+                                 float softmax_scale, int32_t window, const void* table, int32_t table_rows,
+                                 int32_t rotary_dim, void* out, const int64_t o_strides[2], void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
+  DecodeParams p;
+  memset(&p, 0, sizeof p);
+  gptoss_status st = decode_args(p, num_seqs, num_q_heads, num_kv_heads, head_dim, q, q_strides, k_cache, v_cache,
+                                 cache_seqlens, max_cache_len, sinks, softmax_scale, window, table, table_rows,
+                                 rotary_dim, out, o_strides, num_splits);
+  if (st != GPTOSS_OK || num_seqs == 0) return st;
+  if (!kv_strides) return fail(GPTOSS_ERR_NULL, "kv_strides are required");
+  if (!strides_ok(kv_strides, 3))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
+  if (kv_strides[1] < kHeadDim || (int64_t)max_cache_len * kv_strides[1] * 2 > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED,
+                "kv_strides[1] must be >= 64 and one sequence's rows must span less than 2 GiB");
+  p.kind = kCacheContiguous;
+  p.kv_sn = kv_strides[0]; p.kv_sp = kv_strides[1]; p.kv_sh = kv_strides[2];
+  // window layers only ever read the last `window` rows: fewer splits
+  const int32_t eff = (window > 0 && window < max_cache_len) ? window : max_cache_len;
+  return decode_run(p, num_q_heads, eff, max_cache_len, workspace, workspace_bytes, num_splits, stream);
+}
+
+static int ilog2_pow2(int32_t x) {   // log2 of a power of two, else -1
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+// Checks of a cache layout shared by append and decode.
+static gptoss_status check_layout(const gptoss_kv_layout* lay, int32_t max_seqlen, bool for_decode,
+                                  int32_t window) {
+  if (!lay) return fail(GPTOSS_ERR_NULL, "cache layout is NULL");
+  if (lay->kind != GPTOSS_CACHE_CONTIGUOUS && lay->kind != GPTOSS_CACHE_PAGED && lay->kind != GPTOSS_CACHE_RING)
+    return fail(GPTOSS_ERR_SHAPE, "cache kind %d is not CONTIGUOUS (0), PAGED (1) or RING (2)", lay->kind);
+  if (lay->capacity < 1) return fail(GPTOSS_ERR_SHAPE, "cache capacity must be >= 1");
+  if (!strides_ok(lay->strides, 3) || lay->strides[1] < kHeadDim)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "cache strides must be multiples of 8 elements, the row stride >= 64");
+  if ((int64_t)lay->capacity * lay->strides[1] * 2 > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "one sequence's (or page's) rows must span less than 2 GiB");
+  if (lay->kind == GPTOSS_CACHE_PAGED) {
+    if (ilog2_pow2(lay->capacity) < 5)
+      return fail(GPTOSS_ERR_UNSUPPORTED, "page size %d must be a power of two >= 32", lay->capacity);
+    if (!lay->block_table) return fail(GPTOSS_ERR_NULL, "a paged cache needs its block table");
+    if (lay->max_pages < 1 || lay->num_pages < 1)
+      return fail(GPTOSS_ERR_SHAPE, "a paged cache needs max_pages >= 1 and num_pages >= 1");
+    if (for_decode && (int64_t)max_seqlen > (int64_t)lay->max_pages * lay->capacity)
+      return fail(GPTOSS_ERR_SHAPE, "max_seqlen %d exceeds max_pages x page size", max_seqlen);
+  } else if (lay->kind == GPTOSS_CACHE_CONTIGUOUS) {
+    if (for_decode && max_seqlen > lay->capacity)
+      return fail(GPTOSS_ERR_SHAPE, "max_seqlen %d exceeds the cache's %d rows", max_seqlen, lay->capacity);
+  } else if (for_decode && window != lay->capacity) {
+    return fail(GPTOSS_ERR_UNSUPPORTED, "a ring cache serves a window layer with window == capacity (%d, got %d)",
+                lay->capacity, window);
+  }
+  return GPTOSS_OK;
+}
+
+// Most keys one sequence's decode reads from a cache of this layout.
+static int32_t decode_max_keys(const gptoss_kv_layout* lay, int32_t max_seqlen, int32_t window) {
+  if (lay->kind == GPTOSS_CACHE_RING) return std::min(lay->capacity, max_seqlen);
+  if (lay->kind == GPTOSS_CACHE_PAGED) return window > 0 ? std::min(window + 31, max_seqlen) : max_seqlen;
+  return (window > 0 && window < max_seqlen) ? window : max_seqlen;
+}
+
+size_t gptoss_attn_decode_kv_workspace_size(const gptoss_kv_layout* layout, int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t max_seqlen, int32_t window, int32_t num_splits) {
+  if (!layout || num_seqs < 0 || num_q_heads < 0 || max_seqlen < 1 || num_splits < 0 || window < 0) return 0;
+  return decode_ws_bytes(num_seqs, num_q_heads, decode_max_keys(layout, max_seqlen, window), num_splits);
+}
+
+gptoss_status gptoss_attn_decode_kv(const gptoss_kv_layout* layout, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, const void* q,
+                                    const int64_t q_strides[2], const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_seqlens, int32_t max_seqlen, const float* sinks,
+                                    float softmax_scale, int32_t window, const void* table, int32_t table_rows,
+                                    int32_t rotary_dim, void* out, const int64_t o_strides[2], void* workspace,
+                                    size_t workspace_bytes, int32_t num_splits, void* stream) {
+  DecodeParams p;
+  memset(&p, 0, sizeof p);
+  gptoss_status st = decode_args(p, num_seqs, num_q_heads, num_kv_heads, head_dim, q, q_strides, k_cache, v_cache,
+                                 cache_seqlens, max_seqlen, sinks, softmax_scale, window, table, table_rows,
+                                 rotary_dim, out, o_strides, num_splits);
+  if (st != GPTOSS_OK) return st;
+  st = check_layout(layout, max_seqlen, true, window);
+  if (st != GPTOSS_OK || num_seqs == 0) return st;
+  p.kind = layout->kind;
+  p.kv_sn = layout->strides[0]; p.kv_sp = layout->strides[1]; p.kv_sh = layout->strides[2];
+  if (layout->kind == GPTOSS_CACHE_PAGED) {
+    p.page_log2 = ilog2_pow2(layout->capacity);
+    p.block_table = layout->block_table;
+    p.max_pages = layout->max_pages;
+    p.num_pages = layout->num_pages;
+  } else if (layout->kind == GPTOSS_CACHE_RING) {
+    p.ring_slots = layout->capacity;
+  }
+  const int32_t keys = decode_max_keys(layout, max_seqlen, window);
+  return decode_run(p, num_q_heads, keys, keys, workspace, workspace_bytes, num_splits, stream);
+}
+
+gptoss_status gptoss_kv_append(const gptoss_kv_layout* layout, void* k_cache, void* v_cache, int32_t num_seqs,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t num_new, const void* k_new,
+                               const int64_t kn_strides[3], const void* v_new, const int64_t vn_strides[3],
+                               const int32_t* cache_seqlens, int32_t max_seqlen, const void* table,
+                               int32_t table_rows, int32_t rotary_dim, void* stream) {
+  if (num_seqs < 0 || num_new < 0 || max_seqlen < 0) return fail(GPTOSS_ERR_SHAPE, "negative size");
+  if (head_dim != kHeadDim) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", head_dim);
+  if (num_kv_heads < 1) return fail(GPTOSS_ERR_SHAPE, "num_kv_heads must be >= 1");
+  gptoss_status st = check_layout(layout, max_seqlen, false, 0);
+  if (st != GPTOSS_OK) return st;
+  if (num_seqs == 0 || num_new == 0) return GPTOSS_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !kn_strides || !vn_strides || !cache_seqlens)
+    return fail(GPTOSS_ERR_NULL, "caches, new k / v, their strides and cache_seqlens are required");
+  if (!strides_ok(kn_strides, 3) || !strides_ok(vn_strides, 3) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(k_new) || !aligned16(v_new))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
+  st = check_table(table, table_rows, rotary_dim, std::max(max_seqlen, 1));
+  if (st != GPTOSS_OK) return st;
+  AppendParams p;
+  memset(&p, 0, sizeof p);
+  p.k = static_cast<uint16_t*>(k_cache);
+  p.v = static_cast<uint16_t*>(v_cache);
+  p.c_s0 = layout->strides[0]; p.c_sr = layout->strides[1]; p.c_sh = layout->strides[2];
+  p.kind = layout->kind;
+  p.capacity = layout->capacity;
+  if (layout->kind == GPTOSS_CACHE_PAGED) {
+    p.page_log2 = ilog2_pow2(layout->capacity);
+    p.block_table = layout->block_table;
+    p.max_pages = layout->max_pages;
+    p.num_pages = layout->num_pages;
+  }
+  p.kn = static_cast<const uint16_t*>(k_new);
+  p.kn_sn = kn_strides[0]; p.kn_st = kn_strides[1]; p.kn_sh = kn_strides[2];
+  p.vn = static_cast<const uint16_t*>(v_new);
+  p.vn_sn = vn_strides[0]; p.vn_st = vn_strides[1]; p.vn_sh = vn_strides[2];
+  p.cache_seqlens = cache_seqlens;
+  p.num_seqs = num_seqs;
+  p.num_new = num_new;
+  p.num_kv_heads = num_kv_heads;
+  p.table = static_cast<const uint16_t*>(table);
+  p.table_rows = table_rows;
+  return hip_status(launch_kv_append(p, static_cast<hipStream_t>(stream)), "KV append kernel");
 }
 
 }  // extern "C"

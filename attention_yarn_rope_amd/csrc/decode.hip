@@ -44,7 +44,30 @@ __device__ __forceinline__ float col_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <bool ROTQ>
+// The keys of sequence n: the query sits at position L - 1 (L = its clamped
+// length); keys [start, end) are read and those before lo are masked. A
+// contiguous cache reads exactly the visible positions. A paged cache starts at
+// the 32-key boundary at or before lo, so that every 32-key step lies inside
+// one page (pages hold a power of two >= 32 rows). A ring holds the last
+// ring_slots positions in slots 0 .. min(L, ring_slots) - 1, all visible (the
+// window equals the slot count), and the order of keys does not change the
+// result.
+struct KeySpan { int L, lo, start, end; };
+__device__ __forceinline__ KeySpan key_span(const DecodeParams& p, int n) {
+  KeySpan r;
+  r.L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
+  if (p.kind == kCacheRing) {
+    r.lo = r.start = 0;
+    r.end = min(r.L, p.ring_slots);
+  } else {
+    r.lo = (p.window > 0) ? max(0, r.L - p.window) : 0;
+    r.start = (p.kind == kCachePaged) ? (r.lo & ~(SUB - 1)) : r.lo;
+    r.end = r.L;
+  }
+  return r;
+}
+
+template <bool ROTQ, bool PAGED>
 __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[NW][SUB * DVS];
 
@@ -60,10 +83,10 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   const int2 w = direct ? make_int2(it, 0) : work[it];
   const int n = __builtin_amdgcn_readfirstlane(w.x);
   const int split = __builtin_amdgcn_readfirstlane(w.y);
-  const int L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
-  const int lo = (p.window > 0) ? max(0, L - p.window) : 0;
-  const int c0 = lo + split * chunk;
-  const int c1 = min(c0 + chunk, L);
+  const KeySpan span = key_span(p, n);
+  const int L = span.L, lo = span.lo;
+  const int c0 = span.start + split * chunk;
+  const int c1 = min(c0 + chunk, span.end);
   const float sl = p.scale_log2;
 
   const char* kbase = reinterpret_cast<const char*>(p.k + (int64_t)n * p.kv_sn + (int64_t)g * p.kv_sh);
@@ -79,14 +102,33 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   // read as zeros.
   uint4 kr[4], vr[4];
   auto load_block = [&](int s0) __attribute__((always_inline)) {
-    const int64_t start = (int64_t)s0 * row_bytes;
-    const int32_t bytes = (c1 > s0) ? (c1 - s0 - 1) * row_bytes + 2 * kHeadDim : 0;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + start, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + start, bytes);
+    if (PAGED) {
+      // the step lies inside one page: its rows start at row s0 mod page_size of
+      // the page the block table names; rows past c1 and rows before lo (the
+      // 32-key boundary below a window's first key) read as zeros
+      const int lp = s0 >> p.page_log2;
+      const int pid = min(max(__ldg(p.block_table + (int64_t)n * p.max_pages + min(lp, p.max_pages - 1)), 0),
+                          p.num_pages - 1);
+      const int64_t at = (int64_t)pid * p.kv_sn + (int64_t)(s0 - (lp << p.page_log2)) * p.kv_sp;
+      const int32_t bytes = (c1 > s0) ? (min(c1 - s0, SUB) - 1) * row_bytes + 2 * kHeadDim : 0;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + at + (int64_t)g * p.kv_sh, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + at + (int64_t)g * p.kv_sh, bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = ldb16_nt(rk, roff + (uint32_t)(i * 8 * row_bytes));
-      vr[i] = ldb16_nt(rv, roff + (uint32_t)(i * 8 * row_bytes));
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (s0 + (lane >> 3) + 8 * i < lo) ? 0x80000000u : roff + (uint32_t)(i * 8 * row_bytes);
+        kr[i] = ldb16_nt(rk, off);
+        vr[i] = ldb16_nt(rv, off);
+      }
+    } else {
+      const int64_t start = (int64_t)s0 * row_bytes;
+      const int32_t bytes = (c1 > s0) ? (c1 - s0 - 1) * row_bytes + 2 * kHeadDim : 0;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + start, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + start, bytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kr[i] = ldb16_nt(rk, roff + (uint32_t)(i * 8 * row_bytes));
+        vr[i] = ldb16_nt(rv, roff + (uint32_t)(i * 8 * row_bytes));
+      }
     }
   };
   // the first step's rows are requested before q, so both latencies overlap
@@ -147,7 +189,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = s0 + kb * 16 + 4 * grp + r;
-        sacc[kb][r] = (key < c1) ? sacc[kb][r] : -INFINITY;
+        sacc[kb][r] = ((uint32_t)(key - lo) < (uint32_t)(c1 - lo)) ? sacc[kb][r] : -INFINITY;
         mx = fmaxf(mx, sacc[kb][r]);
       }
     mx = col_max(mx);
@@ -213,8 +255,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams 
   __shared__ int chunk_s;
   const int t = threadIdx.x;
   auto eff_len = [&](int n) {
-    const int L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
-    return (p.window > 0) ? min(L, p.window) : L;
+    const KeySpan r = key_span(p, n);
+    return r.end - r.start;
   };
   long long total = 0;
   for (int n = t; n < p.num_seqs; n += kPlanThreads) total += eff_len(n);
@@ -281,10 +323,9 @@ __global__ __launch_bounds__(NTC) void decode_combine_kernel(DecodeParams p) {
   const int n = idx / Hq;
   const int h = idx - n * Hq;
   const int g = h / kGroup, c = h - g * kGroup;
-  const int L = min(max(__ldg(p.cache_seqlens + n), 0), p.max_cache_len);
-  const int lo = (p.window > 0) ? max(0, L - p.window) : 0;
+  const KeySpan span = key_span(p, n);
   const int chunk = p.direct_chunk > 0 ? p.direct_chunk : *p.plan;
-  const int nsplit = min((L - lo + chunk - 1) / chunk, p.num_splits);
+  const int nsplit = min((span.end - span.start + chunk - 1) / chunk, p.num_splits);
   const float sig = __ldg(p.sinks + h) * kLog2e;
   const int64_t base = ((int64_t)n * p.num_kv_heads + g) * p.num_splits;
   float M = sig;
@@ -338,10 +379,13 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   }
   // one work group per planned item (at most max_items of them), looping if there are more
   dim3 grid((unsigned)p.max_items, 1, (p.num_kv_heads + NW - 1) / NW);
+  const bool paged = p.kind == kCachePaged;
   if (p.table)
-    hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((paged ? decode_split_kernel<true, true> : decode_split_kernel<true, false>), grid, dim3(NT),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((paged ? decode_split_kernel<false, true> : decode_split_kernel<false, false>), grid,
+                       dim3(NT), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = p.num_seqs * p.num_kv_heads * kGroup;

@@ -115,8 +115,32 @@ struct DecodeParams {
   float* part_o;                 // [N, Hkv, splits, 8, 64]
   float* part_ml;                // [N, Hkv, splits, 8, 2]
   uint16_t* o; int64_t o_sn, o_sh;
+  // cache layout (kCacheContiguous: kv_sn = sequence stride; kCachePaged: kv_sn =
+  // page stride, rows per page = 1 << page_log2; kCacheRing: ring_slots rows per
+  // sequence, the visible positions of a window layer with window == ring_slots)
+  int32_t kind;
+  int32_t page_log2;
+  int32_t ring_slots;
+  const int32_t* block_table;    // [num_seqs, max_pages]
+  int32_t max_pages, num_pages;
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+constexpr int kCacheContiguous = 0, kCachePaged = 1, kCacheRing = 2;   // gptoss_cache_kind
+
+// ---- KV append ----
+struct AppendParams {
+  uint16_t* k; uint16_t* v; int64_t c_s0, c_sr, c_sh;   // cache strides: sequence or page, row, head
+  int32_t kind, capacity, page_log2;
+  const int32_t* block_table;
+  int32_t max_pages, num_pages;
+  const uint16_t* kn; int64_t kn_sn, kn_st, kn_sh;
+  const uint16_t* vn; int64_t vn_sn, vn_st, vn_sh;
+  const int32_t* cache_seqlens;
+  int32_t num_seqs, num_new, num_kv_heads;
+  const uint16_t* table;         // NULL: k stored as given
+  int32_t table_rows;
+};
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 constexpr int kDecodeMinChunk = 512;   // smallest planned split (keys)
 
 }  // namespace gptoss

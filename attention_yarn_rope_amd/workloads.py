@@ -10,6 +10,8 @@ Generation recipe (one torch.Generator per workload, seeded, in this order):
      for a decode KV cache, sequence by sequence, K rows then V rows of the
      valid length only (rows past the length stay zero);
   3. sinks: torch.randn(num_q_heads, dtype=float32).
+Paged pools, ring caches and appended tokens have their own draw orders (see
+paged_decode, ring_decode, new_tokens).
 
 The shapes follow GPT-OSS's attention: 64 query heads and 8 KV heads of width
 64 (q_proj 2880->4096, k_proj / v_proj 2880->512 in the gpt-oss-20b module
@@ -108,6 +110,63 @@ def decode(num_seqs, lo, hi, seed, max_len=None, hq=HQ, hkv=HKV, d=HEAD_DIM, len
                   lengths=lengths)
 
 
+@dataclass
+class PagedDecode:
+    name: str
+    q: torch.Tensor                  # [N,Hq,D] bf16, un-rotated
+    k_pool: torch.Tensor             # [num_pages, page_size, Hkv, D] bf16, every row random
+    v_pool: torch.Tensor
+    block_table: torch.Tensor        # int32 [N, max_pages]: a random permutation of the used pages
+    cache_seqlens: torch.Tensor      # int32 [N]
+    sinks: torch.Tensor
+    lengths: list = field(default_factory=list)
+
+
+def paged_decode(lengths, page_size, seed, spare_pages=3, hq=HQ, hkv=HKV, d=HEAD_DIM, name=None):
+    """A decode batch over a paged KV pool. Sequence n owns ceil(L_n / page_size)
+    pages (at least one); the pool holds those plus `spare_pages` unused ones, in
+    an order drawn by torch.randperm, and block-table entries past a sequence's
+    pages name page 0. Draw order: q, the K pool, the V pool, the permutation, sinks."""
+    g = torch.Generator().manual_seed(seed)
+    lengths = [int(x) for x in lengths]
+    N = len(lengths)
+    pages = [max(1, -(-L // page_size)) for L in lengths]
+    total = sum(pages) + spare_pages
+    q = _randn_bf16((N, hq, d), g)
+    kp = _randn_bf16((total, page_size, hkv, d), g)
+    vp = _randn_bf16((total, page_size, hkv, d), g)
+    perm = torch.randperm(total, generator=g)
+    bt = torch.zeros((N, max(pages)), dtype=torch.int32)
+    at = 0
+    for n, c in enumerate(pages):
+        bt[n, :c] = perm[at:at + c].to(torch.int32)
+        at += c
+    sinks = torch.randn(hq, generator=g, dtype=torch.float32)
+    return PagedDecode(name or f"paged_N{N}_P{page_size}", q, kp, vp, bt, torch.tensor(lengths, dtype=torch.int32),
+                       sinks, lengths=lengths)
+
+
+def ring_decode(lengths, slots, seed, hq=HQ, hkv=HKV, d=HEAD_DIM, name=None):
+    """A decode batch over ring caches of `slots` rows per sequence (all rows
+    random); lengths are logical and may exceed the slot count. Draw order: q,
+    K rings, V rings, sinks."""
+    g = torch.Generator().manual_seed(seed)
+    lengths = [int(x) for x in lengths]
+    N = len(lengths)
+    q = _randn_bf16((N, hq, d), g)
+    kc = _randn_bf16((N, slots, hkv, d), g)
+    vc = _randn_bf16((N, slots, hkv, d), g)
+    sinks = torch.randn(hq, generator=g, dtype=torch.float32)
+    return Decode(name or f"ring_N{N}_W{slots}", q, kc, vc, torch.tensor(lengths, dtype=torch.int32), sinks,
+                  lengths=lengths)
+
+
+def new_tokens(num_seqs, num_new, seed, hkv=HKV, d=HEAD_DIM):
+    """k and v of the newest tokens [N, num_new, Hkv, D] (un-rotated k), bf16."""
+    g = torch.Generator().manual_seed(seed)
+    return _randn_bf16((num_seqs, num_new, hkv, d), g), _randn_bf16((num_seqs, num_new, hkv, d), g)
+
+
 def grad_out(shape, seed):
     """Gradient of the loss with respect to the attention output for the
     backward pass: torch.randn(shape) rounded to bfloat16, its own generator."""
@@ -135,6 +194,12 @@ def long_context(seed=3):
 
 def decode64(seed=4):
     return decode(64, 1024, 32768, seed, max_len=32768, name="decode_64seq")
+
+
+def decode64_lengths(seed=4):
+    """The cache lengths of decode64 (its generator's first draw) without its caches."""
+    g = torch.Generator().manual_seed(seed)
+    return [int(x) for x in torch.randint(1024, 32768 + 1, (64,), generator=g).tolist()]
 
 
 # ---- work counts (what the throughput figures divide by) ----

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define GPTOSS_ABI_VERSION 2
+#define GPTOSS_ABI_VERSION 3
 
 typedef enum {
   GPTOSS_OK = 0,
@@ -303,6 +303,93 @@ gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  void* out, const int64_t o_strides[2],
                                  void* workspace, size_t workspace_bytes, int32_t num_splits,
                                  void* stream);
+
+/* ---- KV caches of the decode loop ----
+ * No page specifies a KV cache. The pages' generation loop (model.generate in
+ * the Transformers v4.55.0 release notes, "Welcome GPT OSS") has every new
+ * token attend to the keys and values of all earlier tokens of its sequence
+ * (layers page, GptOssAttention), so a cache is where those are kept between
+ * steps. A cache row holds k rotated at its own position (bf16, exactly as
+ * gptoss_rope_qk rotates k) and v unchanged. Position p of sequence n lives:
+ *   GPTOSS_CACHE_CONTIGUOUS  row p of sequence n:  k[n, p, g, :]
+ *   GPTOSS_CACHE_PAGED       row p mod page_size of physical page
+ *                            block_table[n][p / page_size]:  k[page, row, g, :]
+ *   GPTOSS_CACHE_RING        slot p mod capacity of sequence n:  k[n, slot, g, :]
+ *                            It keeps only the last `capacity` positions: what a
+ *                            sliding-window layer whose window equals the
+ *                            capacity reads (128 slots for GPT-OSS's window
+ *                            layers instead of the whole context).
+ * k and v caches share one layout. Element strides (head_dim contiguous):
+ * CONTIGUOUS and RING {sequence, row, kv head}, PAGED {page, row, kv head}.
+ */
+typedef enum { GPTOSS_CACHE_CONTIGUOUS = 0, GPTOSS_CACHE_PAGED = 1, GPTOSS_CACHE_RING = 2 } gptoss_cache_kind;
+typedef struct {
+  int32_t kind;                 /* gptoss_cache_kind */
+  int32_t capacity;             /* CONTIGUOUS: rows per sequence; RING: slots per sequence;
+                                   PAGED: rows per page, a power of two >= 32 */
+  int64_t strides[3];           /* element strides of k and v as above: multiples of 8, row stride >= 64 */
+  const int32_t* block_table;   /* PAGED: device int32 [num_seqs, max_pages], physical page of each
+                                   logical page; entries are clamped to [0, num_pages). Else NULL. */
+  int32_t max_pages;            /* PAGED: block_table entries per sequence */
+  int32_t num_pages;            /* PAGED: pages in the pool */
+} gptoss_kv_layout;
+
+/*
+ * Store the num_new newest tokens of every sequence in a cache. cache_seqlens
+ * (device int32 [num_seqs]) counts each sequence's tokens including the new
+ * ones, so token t (0-based) of sequence n has position
+ * p = cache_seqlens[n] - num_new + t. k is rotated at p with the table (as
+ * gptoss_rope_qk rotates k: bit-identical; table NULL stores k as given) and
+ * written with v at p's row. Tokens that have no row are skipped: p < 0, p at
+ * or past a contiguous cache's capacity or a paged cache's
+ * max_pages * page_size, and in a ring every token of the call older than the
+ * last `capacity` ones (a later token of the same call takes its slot).
+ *   k_new, v_new: device bf16 [num_seqs, num_new, num_kv_heads, head_dim] with
+ *            element strides {sequence, token, head} in kn_strides / vn_strides.
+ *   max_seqlen: host upper bound of cache_seqlens (checked against table_rows).
+ * Calls that write the same row concurrently (the same position twice, or two
+ * positions of a ring slot in different calls on different streams) race.
+ * Errors: GPTOSS_ERR_NULL for missing pointers, GPTOSS_ERR_SHAPE for negative
+ * sizes or a bad kind, GPTOSS_ERR_UNSUPPORTED for head_dim != 64, an unaligned
+ * pointer or stride, a table that does not cover max_seqlen, or a paged page
+ * size that is not a power of two >= 32.
+ */
+gptoss_status gptoss_kv_append(const gptoss_kv_layout* layout, void* k_cache, void* v_cache,
+                               int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t num_new,
+                               const void* k_new, const int64_t kn_strides[3],
+                               const void* v_new, const int64_t vn_strides[3],
+                               const int32_t* cache_seqlens, int32_t max_seqlen,
+                               const void* table, int32_t table_rows, int32_t rotary_dim, void* stream);
+
+/*
+ * gptoss_attn_decode over a cache of any layout: the token at position
+ * cache_seqlens[n] - 1 of every sequence attends to the positions the mask
+ * allows (all earlier positions, or the last min(L, window)), each read from
+ * wherever the layout keeps it. Arguments as for gptoss_attn_decode, plus:
+ *   layout:     the cache layout (above); k_cache / v_cache point at row 0 of
+ *               sequence 0 (CONTIGUOUS, RING) or at page 0 (PAGED).
+ *   max_seqlen: host upper bound of cache_seqlens; it must not exceed a
+ *               contiguous cache's capacity or a paged cache's
+ *               max_pages * page_size. Device lengths above it are clamped.
+ * A RING cache requires window == capacity (it holds exactly the visible
+ * positions). A PAGED decode of a window layer reads from the 32-key boundary
+ * at or before the window's first key; the rows in between are loaded as
+ * zeros, so they need no valid contents.
+ * The workspace size depends on the layout and the window.
+ */
+size_t gptoss_attn_decode_kv_workspace_size(const gptoss_kv_layout* layout, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t max_seqlen, int32_t window,
+                                            int32_t num_splits);
+gptoss_status gptoss_attn_decode_kv(const gptoss_kv_layout* layout, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    const void* q, const int64_t q_strides[2],
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_seqlens, int32_t max_seqlen,
+                                    const float* sinks, float softmax_scale, int32_t window,
+                                    const void* table, int32_t table_rows, int32_t rotary_dim,
+                                    void* out, const int64_t o_strides[2],
+                                    void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

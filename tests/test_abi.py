@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from attention_yarn_rope_amd import _lib
-from attention_yarn_rope_amd._lib import I64x2, I64x3, RopeConfig, SeqDesc
+from attention_yarn_rope_amd._lib import I64x2, I64x3, KVLayout, RopeConfig, SeqDesc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gptoss_attn.h")
@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.gptoss_abi_version() == 2
+    assert lib.gptoss_abi_version() == 3
     for code in range(6):
         assert lib.gptoss_status_string(code)
     assert lib.gptoss_status_string(99) == b"unknown status"
@@ -233,3 +233,79 @@ def test_prefill_lse_requires_lse(lib):
                                      I64x3(128 * 8 * 64, 8 * 64, 64), P, I64x3(128 * 8 * 64, 8 * 64, 64), P, 0.125, 0,
                                      P, 128, 64, P, I64x3(128 * 64 * 64, 64 * 64, 64), None, P, 1 << 30, None)
     assert st == ERR_NULL
+
+
+def _layout(kind=0, cap=1024, strides=(1024 * 8 * 64, 8 * 64, 64), bt=None, max_pages=0, num_pages=0):
+    lay = KVLayout()
+    lay.kind, lay.capacity, lay.strides = kind, cap, I64x3(*strides)
+    lay.block_table, lay.max_pages, lay.num_pages = bt, max_pages, num_pages
+    return lay
+
+
+def _append(lib, lay, **kw):
+    a = dict(k=P, v=P, n=4, hkv=8, d=64, t=1, kn=P, kns=I64x3(8 * 64, 8 * 64, 64), vn=P, vns=I64x3(8 * 64, 8 * 64, 64),
+             lens=P, maxlen=1024, table=P, rows=1024, rd=64)
+    a.update(kw)
+    return lib.gptoss_kv_append(ctypes.byref(lay) if lay is not None else None, a["k"], a["v"], a["n"], a["hkv"],
+                                a["d"], a["t"], a["kn"], a["kns"], a["vn"], a["vns"], a["lens"], a["maxlen"],
+                                a["table"], a["rows"], a["rd"], None)
+
+
+def test_kv_append_argument_errors(lib):
+    assert _append(lib, None) == ERR_NULL
+    assert _append(lib, _layout(kind=3)) == ERR_SHAPE
+    assert _append(lib, _layout(cap=0)) == ERR_SHAPE
+    assert _append(lib, _layout(), d=128) == ERR_UNSUPPORTED
+    assert _append(lib, _layout(), t=-1) == ERR_SHAPE
+    assert _append(lib, _layout(strides=(1024 * 8 * 64, 8 * 64, 65))) == ERR_UNSUPPORTED
+    assert _append(lib, _layout(kind=1, cap=48, bt=P, max_pages=4, num_pages=8)) == ERR_UNSUPPORTED   # page size
+    assert _append(lib, _layout(kind=1, cap=16, bt=P, max_pages=4, num_pages=8)) == ERR_UNSUPPORTED   # below 32
+    assert _append(lib, _layout(kind=1, cap=64, bt=None, max_pages=4, num_pages=8)) == ERR_NULL
+    assert _append(lib, _layout(kind=1, cap=64, bt=P, max_pages=0, num_pages=8)) == ERR_SHAPE
+    assert _append(lib, _layout(), kn=None) == ERR_NULL
+    assert _append(lib, _layout(), lens=None) == ERR_NULL
+    assert _append(lib, _layout(), kns=I64x3(8 * 64, 8 * 64, 60)) == ERR_UNSUPPORTED
+    assert _append(lib, _layout(), rows=100) == ERR_SHAPE          # table shorter than max_seqlen
+    assert _append(lib, _layout(), t=0) == OK
+    assert _append(lib, _layout(), n=0) == OK
+
+
+def _decode_kv(lib, lay, **kw):
+    a = dict(n=4, hq=64, hkv=8, d=64, q=P, qs=I64x2(64 * 64, 64), k=P, v=P, lens=P, maxlen=1024, sinks=P,
+             scale=0.125, window=0, table=P, rows=1024, rd=64, out=P, os=I64x2(64 * 64, 64), ws=P, wsb=1 << 30,
+             splits=0)
+    a.update(kw)
+    return lib.gptoss_attn_decode_kv(ctypes.byref(lay) if lay is not None else None, a["n"], a["hq"], a["hkv"],
+                                     a["d"], a["q"], a["qs"], a["k"], a["v"], a["lens"], a["maxlen"], a["sinks"],
+                                     a["scale"], a["window"], a["table"], a["rows"], a["rd"], a["out"], a["os"],
+                                     a["ws"], a["wsb"], a["splits"], None)
+
+
+def test_decode_kv_argument_errors(lib):
+    assert _decode_kv(lib, None) == ERR_NULL
+    assert _decode_kv(lib, _layout(), maxlen=2048, rows=4096) == ERR_SHAPE            # beyond the cache's rows
+    assert _decode_kv(lib, _layout(kind=2, cap=128), window=0) == ERR_UNSUPPORTED    # ring needs window = capacity
+    assert _decode_kv(lib, _layout(kind=2, cap=128), window=64) == ERR_UNSUPPORTED
+    paged = _layout(kind=1, cap=64, strides=(64 * 8 * 64, 8 * 64, 64), bt=P, max_pages=8, num_pages=100)
+    assert _decode_kv(lib, paged, maxlen=1024) == ERR_SHAPE                          # 8 pages x 64 rows = 512
+    assert _decode_kv(lib, _layout(kind=1, cap=100, bt=P, max_pages=8, num_pages=9), maxlen=512) == ERR_UNSUPPORTED
+    assert _decode_kv(lib, paged, maxlen=512, wsb=16) == ERR_WORKSPACE
+    assert _decode_kv(lib, _layout(), d=128) == ERR_UNSUPPORTED
+    assert _decode_kv(lib, _layout(), lens=None) == ERR_NULL
+    assert _decode_kv(lib, _layout(kind=2, cap=128), window=128, wsb=16) == ERR_WORKSPACE
+    assert _decode_kv(lib, _layout(), n=0) == OK
+
+
+def test_decode_kv_workspace_size(lib):
+    # contiguous == the plain decode's size; a ring is sized by its slots; a paged window
+    # layer by window + 31 keys (its reads start at a 32-key boundary)
+    cont = _layout(cap=32768)
+    assert lib.gptoss_attn_decode_kv_workspace_size(ctypes.byref(cont), 64, 64, 32768, 0, 0) == \
+        lib.gptoss_attn_decode_workspace_size(64, 64, 32768, 0)
+    ring = _layout(kind=2, cap=128)
+    assert lib.gptoss_attn_decode_kv_workspace_size(ctypes.byref(ring), 64, 64, 1 << 20, 128, 0) == \
+        lib.gptoss_attn_decode_workspace_size(64, 64, 128, 0)
+    paged = _layout(kind=1, cap=64, bt=P, max_pages=512, num_pages=4096)
+    assert lib.gptoss_attn_decode_kv_workspace_size(ctypes.byref(paged), 64, 64, 32768, 128, 0) == \
+        lib.gptoss_attn_decode_workspace_size(64, 64, 159, 0)
+    assert lib.gptoss_attn_decode_kv_workspace_size(None, 64, 64, 32768, 0, 0) == 0
