@@ -8,7 +8,9 @@ full-causal layer and one sliding-window-128 layer, each with q and k rotated
 inside the attention call. `value` is unmasked prefill TFLOP/s over the step
 (4 * D * Hq FLOPs per visible (query, key) pair). The decode half of the metric
 (64 sequences, cache lengths uniform in [1024, 32768], full and window-128
-layers) is timed in the same run and reported under "decode".
+layers) is timed in the same run and reported under "decode", with the same
+decode over a paged cache (64-row pages in a shuffled pool) and over 128-slot
+ring caches for the window layer, and the cache append, under "decode.kv_cache".
 
 Timing uses HIP events recorded on the stream the library launches on, around
 every call inside the timed region; the whole region is bracketed by device
@@ -19,7 +21,8 @@ The backward pass of both layers (dq, dk, dv, dsinks) is timed after the step an
 reported under "backward" (not part of `value`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
-       python bench.py --profile {prefill-full,prefill-window,decode-full,copy,backward-full,backward-window} --steps K
+       python bench.py --profile {prefill-full,prefill-window,decode-full,copy,backward-full,backward-window,
+                                  decode-paged,decode-ring,kv-append} --steps K
        (the --profile modes run only the named call, for rocprofv3)
 """
 
@@ -133,6 +136,82 @@ def cpu_baseline(inp, budget_s):
                       f"full-causal and window-128 layers, fp64 numpy on the host CPU"}
 
 
+def kv_cache_calls(torch, gx, wl, dev, dq, kc, vc, lens, dsinks, dtable, lengths, d_out, pk, pv):
+    """Closures over the decode workload's caches in the other layouts.
+
+    paged_full: the full layer over a pool of 64-row pages holding the same rows in a
+    shuffled page order (block table = where each logical page went); ring_window: the
+    window layer over 128-slot ring caches (random rows); append_1: one new token per
+    sequence appended to the paged pool and to the rings; append_prompt: the dense
+    prefill's k and v (B=4 S=4096) appended to a contiguous cache in one call.
+    """
+    N, Lmax = kc.shape[0], kc.shape[1]
+    ps = 64
+    npages = N * Lmax // ps
+    perm = torch.randperm(npages, generator=torch.Generator().manual_seed(12)).to(dev)
+    k_pool = torch.empty((npages, ps, 8, 64), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty_like(k_pool)
+    k_pool[perm] = kc.reshape(npages, ps, 8, 64)
+    v_pool[perm] = vc.reshape(npages, ps, 8, 64)
+    block_table = perm.to(torch.int32).reshape(N, Lmax // ps).contiguous()
+    ring = wl.ring_decode(lengths, 128, seed=45)
+    rk, rv = ring.k_cache.to(dev), ring.v_cache.to(dev)
+    kn, vn = (t.to(dev) for t in wl.new_tokens(N, 1, 46))
+    pws = torch.empty(gx.decode_kv_workspace_size(dq, k_pool, "paged", block_table, 0, Lmax), dtype=torch.uint8,
+                      device=dev)
+    rws = torch.empty(gx.decode_kv_workspace_size(dq, rk, "ring", None, 128, Lmax), dtype=torch.uint8, device=dev)
+    ptable = gx.rope_table(pk.shape[1])
+    ck = torch.empty_like(pk)
+    cv = torch.empty_like(pv)
+    plens = torch.full((pk.shape[0],), pk.shape[1], dtype=torch.int32, device=dev)
+    out = torch.empty_like(d_out)
+
+    def append_1():
+        gx.kv_append(k_pool, v_pool, kn, vn, lens, kind="paged", block_table=block_table, table=dtable,
+                     max_seqlen=Lmax)
+        gx.kv_append(rk, rv, kn, vn, lens, kind="ring", table=dtable, max_seqlen=Lmax)
+
+    return {
+        "paged_full": lambda: gx.attn_decode_kv(dq, k_pool, v_pool, lens, dsinks, kind="paged",
+                                                block_table=block_table, table=dtable, max_seqlen=Lmax, out=out,
+                                                workspace=pws),
+        "ring_window": lambda: gx.attn_decode_kv(dq, rk, rv, lens, dsinks, kind="ring", window=128, table=dtable,
+                                                 max_seqlen=Lmax, out=out, workspace=rws),
+        "append_1": append_1,
+        "append_prompt": lambda: gx.kv_append(ck, cv, pk, pv, plens, table=ptable),
+        "prompt_tokens": pk.shape[0] * pk.shape[1],
+    }
+
+
+def kv_cache_bench(torch, wl, kvc, args, lengths, b_full, b_win):
+    timer = Timer(torch)
+    names = ("paged_full", "ring_window", "append_1", "append_prompt")
+    for _ in range(args.warmup):
+        for n in names:
+            kvc[n]()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        for n in names:
+            timer.run(n, kvc[n])
+    torch.cuda.synchronize()
+    ms = {n: timer.mean_ms(n) for n in names}
+    T = kvc["prompt_tokens"]
+    b_prompt = T * 8 * 64 * 2 * 4 + 4096 * 64 * 2   # read k, v; write k, v; table rows
+    return {
+        "workload": "the decode workload's caches as a shuffled pool of 64-row pages (full layer) and as 128-slot "
+                    "ring caches (window layer); append: 1 token x 64 sequences into the pool and the rings, and "
+                    f"a {T}-token prompt (B=4 S=4096) into a contiguous cache",
+        "paged_full_layer": {"ms": round(ms["paged_full"], 4),
+                             "GB/s": round(b_full / (ms["paged_full"] * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(b_full / (ms["paged_full"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "ring_window_layer": {"ms": round(ms["ring_window"], 4),
+                              "GB/s": round(b_win / (ms["ring_window"] * 1e-3) / 1e9, 1)},
+        "append_1_token_ms": round(ms["append_1"], 4),
+        "append_prompt": {"ms": round(ms["append_prompt"], 4), "bytes": b_prompt,
+                          "GB/s": round(b_prompt / (ms["append_prompt"] * 1e-3) / 1e9, 1)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,7 +223,8 @@ def main():
     ap.add_argument("--k-rotation", default="auto", choices=["auto", "fused", "separate"])
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy",
-                                                        "backward-full", "backward-window"])
+                                                        "backward-full", "backward-window", "decode-paged",
+                                                        "decode-ring", "kv-append"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -275,7 +355,7 @@ def main():
 
     # ---------------- decode ----------------
     decode_obj = None
-    if not args.no_decode or args.profile == "decode-full":
+    if not args.no_decode or args.profile in ("decode-full", "decode-paged", "decode-ring", "kv-append"):
         log("[bench] generating decode workload: 64 sequences, lengths uniform in [1024, 32768]")
         dinp = wl.decode64()
         dq = dinp.q.to(dev)
@@ -297,6 +377,14 @@ def main():
                 dec(0)()
             torch.cuda.synchronize()
             log(f"decode-full: {args.steps} launches")
+            return
+        kvc = kv_cache_calls(torch, gx, wl, dev, dq, kc, vc, lens, dsinks, dtable, dinp.lengths, d_out, k, v)
+        if args.profile in ("decode-paged", "decode-ring", "kv-append"):
+            fn = kvc[{"decode-paged": "paged_full", "decode-ring": "ring_window", "kv-append": "append_1"}[args.profile]]
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            log(f"{args.profile}: {args.steps} launches")
             return
         timer = Timer(torch)
         for _ in range(args.warmup):
@@ -321,7 +409,8 @@ def main():
             "traffic": counters_traffic("decode_full_64seq", "decode"),
         }
         log(f"[bench] decode full {ms_df:.3f} ms = {gbs:.0f} GB/s; window {ms_dw:.4f} ms")
-        del kc, vc
+        decode_obj["kv_cache"] = kv_cache_bench(torch, wl, kvc, args, dinp.lengths, b_full, b_win)
+        del kc, vc, kvc
 
     tflops = (flops_full + flops_win) / (ms_step * 1e-3) / 1e12
     achieved = flops_full / (ms_full * 1e-3) / 1e12
