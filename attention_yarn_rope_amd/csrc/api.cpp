@@ -111,10 +111,20 @@ int32_t thd_max_items(const gptoss_seq_desc* d) {
   return (d->seqlen + kPrefillBQ - 1) / kPrefillBQ + d->batch;
 }
 
-gptoss_status check_table(const void* table, int32_t table_rows, int32_t rotary_dim, int32_t need_rows) {
+// partial: the standalone rotations (gptoss_rope_qk, gptoss_kv_append) rotate
+// the first rotary_dim dims for any multiple of 16 and copy the rest; the
+// attention kernels rotate all 64 dims on their loads.
+gptoss_status check_table(const void* table, int32_t table_rows, int32_t rotary_dim, int32_t need_rows,
+                          bool partial = false) {
   if (!table) return GPTOSS_OK;
-  if (rotary_dim != kHeadDim)
-    return fail(GPTOSS_ERR_UNSUPPORTED, "rotary_dim %d unsupported (only 64 = head_dim)", rotary_dim);
+  if (partial) {
+    if (rotary_dim < 16 || rotary_dim > kHeadDim || rotary_dim % 16 != 0)
+      return fail(GPTOSS_ERR_UNSUPPORTED, "rotary_dim %d unsupported (16, 32, 48 or 64)", rotary_dim);
+  } else if (rotary_dim != kHeadDim) {
+    return fail(GPTOSS_ERR_UNSUPPORTED,
+                "rotary_dim %d: the attention kernels rotate all 64 dims; rotate q and k with gptoss_rope_qk "
+                "and pass table = NULL", rotary_dim);
+  }
   if (!aligned16(table)) return fail(GPTOSS_ERR_UNSUPPORTED, "table must be 16-byte aligned");
   if (table_rows < need_rows || table_rows < 1)
     return fail(GPTOSS_ERR_SHAPE, "table has %d rows, positions up to %d are needed", table_rows, need_rows - 1);
@@ -174,7 +184,7 @@ gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc, const void* q, const i
   if (!strides_ok(q_strides, 3) || !strides_ok(k_strides, 3) || !aligned16(q) || !aligned16(k) ||
       !aligned16(q_out) || !aligned16(k_out))
     return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
-  st = check_table(table, table_rows, rotary_dim, desc_max_len(desc));
+  st = check_table(table, table_rows, rotary_dim, desc_max_len(desc), true);
   if (st != GPTOSS_OK) return st;
   const bool thd = desc->layout == GPTOSS_THD;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -193,6 +203,7 @@ gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc, const void* q, const i
     p.num_seqs = desc->batch;
     p.table = static_cast<const uint16_t*>(table);
     p.table_rows = table_rows;
+    p.rot_chunks = rotary_dim / 16;
     if (thd && desc->batch == 0) return GPTOSS_OK;
     st = hip_status(launch_rope_qk(p, s), "rope_qk kernel");
     if (st != GPTOSS_OK) return st;
@@ -294,6 +305,7 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
     r.num_seqs = desc->batch;
     r.table = p.table;
     r.table_rows = table_rows;
+    r.rot_chunks = kHeadDim / 16;
     st = hip_status(launch_rope_qk(r, s), "k rotation kernel");
     if (st != GPTOSS_OK) return st;
     p.k = krot_buf;
@@ -712,7 +724,7 @@ gptoss_status gptoss_kv_append(const gptoss_kv_layout* layout, void* k_cache, vo
   if (!strides_ok(kn_strides, 3) || !strides_ok(vn_strides, 3) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(k_new) || !aligned16(v_new))
     return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
-  st = check_table(table, table_rows, rotary_dim, std::max(max_seqlen, 1));
+  st = check_table(table, table_rows, rotary_dim, std::max(max_seqlen, 1), true);
   if (st != GPTOSS_OK) return st;
   AppendParams p;
   memset(&p, 0, sizeof p);
@@ -737,6 +749,7 @@ gptoss_status gptoss_kv_append(const gptoss_kv_layout* layout, void* k_cache, vo
   p.num_kv_heads = num_kv_heads;
   p.table = static_cast<const uint16_t*>(table);
   p.table_rows = table_rows;
+  p.rot_chunks = rotary_dim / 16;
   return hip_status(launch_kv_append(p, static_cast<hipStream_t>(stream)), "KV append kernel");
 }
 

@@ -72,8 +72,9 @@ __device__ __forceinline__ bool maybe_inexact_tie(float s, float p, float t) {
          (__builtin_fminf(__builtin_fabsf(p), __builtin_fabsf(t)) < __builtin_fabsf(s) * 0x1p-8f);
 }
 
-// Rotate 8 pairs: x1 holds dims i..i+7, x2 dims i+32..i+39 (rotary_dim 64),
-// c / s the table's cos / sin for the same i. Writes rounded bf16 outputs.
+// Rotate 8 pairs: x1 holds dims i..i+7, x2 their partners i+h..i+h+7 (h =
+// rotary_dim / 2), c / s the table's cos / sin for the same i. Writes rounded
+// bf16 outputs.
 __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const uint4& c,
                                       const uint4& s, uint4& y1, uint4& y2) {
   const uint32_t* px1 = reinterpret_cast<const uint32_t*>(&x1);
@@ -122,6 +123,8 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
     py2[w] = pack_bf16x2(r2[2 * w], r2[2 * w + 1]);
   }
 }
+
+
 
 // ---------------------------------------------------------------------------
 // MFMA v_mfma_f32_16x16x32_bf16 (one wave of 64 lanes):
@@ -173,5 +176,28 @@ __device__ __forceinline__ uint4 ldb16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(bf16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Rotation of one 64-dim row by a table row (cos of the rotary_dim / 2 pairs,
+// then their sin), for the 8-dim chunks c and c + 4 a thread owns. Chunk c <
+// hb (hb = rotary_dim / 16) is rotated together with chunk c + hb, its pair
+// partner, and both results are stored; chunks at or past 2 hb (the partial-
+// rotary tail) are copied; chunks in [hb, 2 hb) are stored by their partner's
+// owner. With rotary_dim = 64 (hb = 4) thread cc rotates chunks cc and cc + 4.
+__device__ __forceinline__ void rotate_row_chunks(const uint16_t* x, uint16_t* y, const uint16_t* tab, int hb,
+                                                  int cc) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = cc + 4 * j;
+    if (c < hb) {
+      const uint4 x1 = ldg16(x + 8 * c), x2 = ldg16(x + 8 * (c + hb));
+      uint4 y1, y2;
+      rope8(x1, x2, ldg16(tab + 8 * c), ldg16(tab + 8 * (c + hb)), y1, y2);
+      stg16(y + 8 * c, y1);
+      stg16(y + 8 * (c + hb), y2);
+    } else if (c >= 2 * hb) {
+      stg16(y + 8 * c, ldg16(x + 8 * c));
+    }
+  }
+}
 
 }  // namespace gptoss

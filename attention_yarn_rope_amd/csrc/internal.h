@@ -28,8 +28,9 @@ struct RopeQKParams {
   int32_t batch, tokens, heads;  // BSHD: batch x seqlen; THD: batch = 1, tokens = T
   const int32_t* cu_seqlens;     // THD positions (NULL for BSHD)
   int32_t num_seqs;
-  const uint16_t* table;
+  const uint16_t* table;         // [table_rows, rotary_dim]: cos of the rotary_dim / 2 pairs, then sin
   int32_t table_rows;
+  int32_t rot_chunks;            // rotary_dim / 16: 8-dim chunks in each half of the rotated part
 };
 hipError_t launch_rope_qk(const RopeQKParams& p, hipStream_t stream);
 
@@ -139,6 +140,7 @@ struct AppendParams {
   int32_t num_seqs, num_new, num_kv_heads;
   const uint16_t* table;         // NULL: k stored as given
   int32_t table_rows;
+  int32_t rot_chunks;            // rotary_dim / 16
 };
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 constexpr int kDecodeMinChunk = 512;   // smallest planned split (keys)

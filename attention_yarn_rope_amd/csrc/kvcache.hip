@@ -14,9 +14,10 @@
 namespace gptoss {
 namespace {
 
-// One thread per (sequence, new token, KV head, 8-pair chunk): dims [8c, 8c+8)
-// and [32+8c, 32+8c+8) of k (rotated together) and of v. Four consecutive
-// threads cover one 128-byte row.
+// One thread per (sequence, new token, KV head, chunk pair cc in 0..3): the
+// 8-dim chunks cc and cc + 4 of v, and of k rotated by rotate_row_chunks (any
+// rotary_dim that is a multiple of 16; the tail past it is copied). Four
+// consecutive threads cover one 128-byte row.
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t rows = (int64_t)p.num_seqs * p.num_new * p.num_kv_heads;
@@ -42,22 +43,18 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     if (pos >= p.capacity) return;
     row = (int64_t)n * p.c_s0 + (int64_t)pos * p.c_sr;
   }
-  row += (int64_t)g * p.c_sh + 8 * cc;
-  const uint16_t* kx = p.kn + (int64_t)n * p.kn_sn + (int64_t)t * p.kn_st + (int64_t)g * p.kn_sh + 8 * cc;
-  const uint16_t* vx = p.vn + (int64_t)n * p.vn_sn + (int64_t)t * p.vn_st + (int64_t)g * p.vn_sh + 8 * cc;
-  uint4 k1 = ldg16(kx), k2 = ldg16(kx + 32);
-  const uint4 v1 = ldg16(vx), v2 = ldg16(vx + 32);
+  row += (int64_t)g * p.c_sh;
+  const uint16_t* kx = p.kn + (int64_t)n * p.kn_sn + (int64_t)t * p.kn_st + (int64_t)g * p.kn_sh;
+  const uint16_t* vx = p.vn + (int64_t)n * p.vn_sn + (int64_t)t * p.vn_st + (int64_t)g * p.vn_sh;
   if (p.table) {
-    const uint16_t* tab = p.table + (int64_t)min(pos, p.table_rows - 1) * kHeadDim + 8 * cc;
-    uint4 y1, y2;
-    rope8(k1, k2, ldg16(tab), ldg16(tab + 32), y1, y2);
-    k1 = y1;
-    k2 = y2;
+    rotate_row_chunks(kx, p.k + row, p.table + (int64_t)min(pos, p.table_rows - 1) * (16 * p.rot_chunks),
+                      p.rot_chunks, cc);
+  } else {
+    stg16(p.k + row + 8 * cc, ldg16(kx + 8 * cc));
+    stg16(p.k + row + 32 + 8 * cc, ldg16(kx + 32 + 8 * cc));
   }
-  stg16(p.k + row, k1);
-  stg16(p.k + row + 32, k2);
-  stg16(p.v + row, v1);
-  stg16(p.v + row + 32, v2);
+  stg16(p.v + row + 8 * cc, ldg16(vx + 8 * cc));
+  stg16(p.v + row + 32 + 8 * cc, ldg16(vx + 32 + 8 * cc));
 }
 
 }  // namespace

@@ -52,9 +52,7 @@ __device__ __forceinline__ int32_t find_seq(const int32_t* cu, int32_t num_seqs,
   return lo;
 }
 
-// One thread per (token row, head, 8-pair chunk): loads dims [8c, 8c+8) and
-// [32+8c, 32+8c+8), the matching cos/sin of the token's position, and writes
-// the 16 rotated values.
+// One thread per (token row, head, chunk pair cc in 0..3).
 __global__ __launch_bounds__(256) void rope_qk_kernel(RopeQKParams p) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t rows = (int64_t)p.batch * p.tokens * p.heads;
@@ -68,15 +66,8 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(RopeQKParams p) {
   int32_t pos = t;
   if (p.cu_seqlens) pos = t - __ldg(p.cu_seqlens + find_seq(p.cu_seqlens, p.num_seqs, t));
   pos = min(max(pos, 0), p.table_rows - 1);
-  const uint16_t* x = p.x + b * p.s_b + t * p.s_t + h * p.s_h + 8 * cc;
-  const uint16_t* tab = p.table + (int64_t)pos * kHeadDim + 8 * cc;
-  uint4 x1 = ldg16(x), x2 = ldg16(x + 32);
-  uint4 c = ldg16(tab), s = ldg16(tab + 32);
-  uint4 y1, y2;
-  rope8(x1, x2, c, s, y1, y2);
-  uint16_t* y = p.y + r * kHeadDim + 8 * cc;
-  stg16(y, y1);
-  stg16(y + 32, y2);
+  const uint16_t* x = p.x + b * p.s_b + t * p.s_t + h * p.s_h;
+  rotate_row_chunks(x, p.y + r * kHeadDim, p.table + (int64_t)pos * (16 * p.rot_chunks), p.rot_chunks, cc);
 }
 
 }  // namespace

@@ -25,9 +25,12 @@
  *     every index derived from it so that bad values cannot read or write
  *     outside the buffers described by the host-side sizes.
  *
- * Supported now: head_dim == rotary_dim == 64, num_q_heads == 8 * num_kv_heads
- * (the GPT-OSS grouping: 64 query heads over 8 KV heads); other shapes return
- * GPTOSS_ERR_UNSUPPORTED.
+ * Supported now: head_dim == 64, num_q_heads == 8 * num_kv_heads (the GPT-OSS
+ * grouping: 64 query heads over 8 KV heads). rotary_dim is 64 for the
+ * attention entry points that take a table; gptoss_rope_qk and
+ * gptoss_kv_append also rotate a partial rotary_dim of 16, 32 or 48 (the dims
+ * past it copied), after which attention runs on the pre-rotated q and k with
+ * table = NULL. Other shapes return GPTOSS_ERR_UNSUPPORTED.
  */
 #ifndef GPTOSS_ATTN_H
 #define GPTOSS_ATTN_H
@@ -136,7 +139,9 @@ gptoss_status gptoss_rope_table_init(const gptoss_rope_config* cfg, int32_t num_
  *   table: from gptoss_rope_table_init, table_rows >= max position + 1.
  * The pair (x[i], x[i + rotary_dim/2]) is multiplied as a complex number by
  * (cos_i + j sin_i) of the token's position row; each output element is the
- * exact result rounded once to bf16; dims >= rotary_dim are copied.
+ * exact result rounded once to bf16; dims >= rotary_dim are copied (partial
+ * rotary, rope_utils page, apply_rotary_emb). rotary_dim: 16, 32, 48 or 64,
+ * the table's width.
  */
 gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc,
                              const void* q, const int64_t q_strides[3],

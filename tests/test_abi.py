@@ -177,6 +177,14 @@ def test_rope_qk_argument_errors(lib):
     assert f(ctypes.byref(d), P, S3, P, K3, P, P, P, 10, 64, None) == ERR_SHAPE
     assert f(ctypes.byref(_desc(head_dim=32)), P, S3, P, K3, P, P, P, 4096, 64, None) == ERR_UNSUPPORTED
     assert f(ctypes.byref(_desc(seqlen=0)), P, S3, P, K3, P, P, P, 4096, 64, None) == OK
+    for rd in (8, 24, 40, 66):   # partial rotary: multiples of 16 only
+        assert f(ctypes.byref(d), P, S3, P, K3, P, P, P, 4096, rd, None) == ERR_UNSUPPORTED
+
+
+def test_attention_needs_full_rotary_with_a_table(lib):
+    # rotary_dim < 64 is served by gptoss_rope_qk + table = NULL, not by the attention kernels
+    assert _prefill(lib, _desc_bshd(), rd=32) == ERR_UNSUPPORTED
+    assert _decode(lib, rd=32) == ERR_UNSUPPORTED
 
 
 def test_prefill_ex_rejects_unknown_k_rotation(lib):

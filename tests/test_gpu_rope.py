@@ -107,3 +107,67 @@ def test_rope_qk_far_positions(table128k):
     assert np.array_equal(np64(qo[0, rows]), rq)
     rk = oracle.rotate(np64(k[0, rows]), cos[:, None, :], sin[:, None, :])
     assert np.array_equal(np64(ko[0, rows]), rk)
+
+
+@pytest.mark.parametrize("rd", [16, 32, 48])
+def test_rope_qk_partial_rotary_bit_exact(rd):
+    """rotary_dim < 64: the first rd dims rotate in pairs (i, i + rd/2), the rest are copied."""
+    cfg = oracle.RopeConfig(rotary_dim=rd)
+    table = gx.rope_table(1100, gx.rope_config(rotary_dim=rd))
+    assert tuple(table.shape) == (1100, rd)
+    # the table is rounded from fp64 sin/cos on both sides; a near-tie entry may round
+    # the other way (at most a couple per 10^5). Positions whose row differs are
+    # left out of the bit-exact comparison.
+    same = (bits16(table) == oracle.bf16_bits(oracle.freqs_cis(cfg, 1100))).all(axis=1)
+    assert int((~same).sum()) <= 2
+    inp = wl.prefill_bshd(2, 1031, seed=300 + rd)
+    say(f"[gpu] rope_qk partial rotary rd={rd} ({int((~same).sum())} table rows differ)")
+    qo, ko = gx.rope_qk(inp.q.cuda(), inp.k.cuda(), table)
+    rq, rk = oracle.rope_qk_bshd(np64(inp.q), np64(inp.k), cfg)
+    keep = same[:1031]
+    assert np.array_equal(np64(qo)[:, keep], rq[:, keep]) and np.array_equal(np64(ko)[:, keep], rk[:, keep])
+    assert torch.equal(qo[..., rd:].cpu(), inp.q[..., rd:])
+    t = wl.prefill_thd(0, 0, 0, seed=310 + rd, lengths=[7, 0, 300, 64])
+    qo, ko = gx.rope_qk(t.q.cuda(), t.k.cuda(), table, cu_seqlens=t.cu_seqlens.cuda(), max_seqlen=t.max_seqlen)
+    rq, rk = oracle.rope_qk_thd(np64(t.q), np64(t.k), t.cu_seqlens.numpy(), cfg)
+    keep = same[oracle.thd_positions(t.cu_seqlens.numpy(), t.q.shape[0])]
+    assert np.array_equal(np64(qo)[keep], rq[keep]) and np.array_equal(np64(ko)[keep], rk[keep])
+
+
+def test_partial_rotary_attention_through_pre_rotation():
+    """Prefill with rotary_dim 32: q and k rotated by rope_qk, then attention with table=None,
+    against the oracle's prefill with the same partial rotary."""
+    from helpers import assert_close
+    cfg = oracle.RopeConfig(rotary_dim=32)
+    table = gx.rope_table(400, gx.rope_config(rotary_dim=32))
+    inp = wl.prefill_bshd(2, 333, seed=320)
+    s = inp.sinks.cuda()
+    qr, kr = gx.rope_qk(inp.q.cuda(), inp.k.cuda(), table)
+    for w in (0, 128):
+        out = gx.attn_prefill(qr, kr, inp.v.cuda(), s, window=w, table=None)
+        ref = oracle.prefill_bshd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.sinks), 0.125, w, cfg)
+        assert_close(out, ref, f"partial rotary rd=32 W={w}")
+    with pytest.raises(Exception):
+        gx.attn_prefill(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), s, window=0, table=table)
+
+
+def test_kv_append_partial_rotary_bit_exact():
+    from oracle import kvcache as kv
+    cfg = oracle.RopeConfig(rotary_dim=32)
+    table = gx.rope_table(200, gx.rope_config(rotary_dim=32))
+    kn, vn = wl.new_tokens(3, 5, 330)
+    kc = torch.zeros((3, 160, 8, 64), dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kg, vg = kc.cuda(), vc.cuda()
+    lens = [5, 77, 160]
+    gx.kv_append(kg, vg, kn.cuda(), vn.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), table=table,
+                 max_seqlen=160)
+    rk, rv = kv.append(kv.KVLayout(kv.CONTIGUOUS, 160), np64(kc), np64(vc), np64(kn), np64(vn), lens, cfg)
+    same = (bits16(table) == oracle.bf16_bits(oracle.freqs_cis(cfg, 200))).all(axis=1)
+    assert int((~same).sum()) <= 2
+    g, r = np64(kg), rk
+    for n, L in enumerate(lens):
+        pos = np.arange(L - 5, L)
+        pos = pos[same[pos]]
+        assert np.array_equal(g[n, pos], r[n, pos])
+    assert np.array_equal(np64(vg), rv)
