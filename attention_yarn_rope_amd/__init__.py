@@ -1,6 +1,7 @@
 """GPT-OSS attention hot path on MI355X: YaRN RoPE, sink + GQA + sliding-window
 prefill (BSHD and packed THD) with its backward pass, split-KV decode over
-contiguous, paged or ring KV caches and the cache append, as
+contiguous, paged or ring KV caches, the cache append, and the q/k/v
+projections with the RoPE in their epilogue, as
 hand-written gfx950 HIP kernels behind a C ABI (include/gptoss_attn.h). This
 package is the thin torch binding; libgptoss_attn.so is loaded on first use and
 is required.
@@ -15,6 +16,7 @@ from .api import (  # noqa: F401
     attn_prefill_lse,
     attn_prefill_backward,
     attn_decode,
+    qkv_proj_rope,
     kv_layout,
     kv_append,
     attn_decode_kv,

@@ -328,3 +328,49 @@ def attn_decode_kv(q, k_cache, v_cache, cache_seqlens, sinks, kind="contiguous",
         _ptr(out), I64x2(out.stride(0), out.stride(1)), _ptr(workspace), workspace.numel(), int(num_splits),
         _stream()))
     return out
+
+
+def qkv_proj_rope(x, wq, bq, wk, bk, wv, bv, table=None, cu_seqlens=None, max_seqlen=None, out=None):
+    """q, k, v = x W^T + b (rounded to bf16), q and k then rotated with the table (None: not rotated).
+
+    x: [B, S, hidden] (BSHD) or [T, hidden] with cu_seqlens (THD); weights [out, hidden] (Linear
+    layout), biases [out] or None. Returns q [.., Hq, 64], k and v [.., Hkv, 64] in x's layout."""
+    _bf16(x, "x")
+    for name, w in (("wq", wq), ("wk", wk), ("wv", wv)):
+        _bf16(w, name)
+        if not w.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, b in (("bq", bq), ("bk", bk), ("bv", bv)):
+        if b is not None:
+            _bf16(b, name)
+    hidden = x.shape[-1]
+    hq, hkv = wq.shape[0] // HEAD_DIM, wk.shape[0] // HEAD_DIM
+    if cu_seqlens is None:
+        if x.dim() != 3:
+            raise ValueError("BSHD x must be [B, S, hidden]")
+        B, S = x.shape[0], x.shape[1]
+        if x.stride(0) != S * x.stride(1):
+            raise ValueError("x's rows must be evenly spaced ([B, S] flattened)")
+        desc = SeqDesc(_lib.BSHD, B, S, S, None, hq, hkv, HEAD_DIM)
+        lead = (B, S)
+    else:
+        if x.dim() != 2:
+            raise ValueError("THD x must be [T, hidden]")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
+            raise TypeError("cu_seqlens must be a contiguous CUDA int32 tensor")
+        T = x.shape[0]
+        if max_seqlen is None:
+            cu = cu_seqlens.cpu()
+            max_seqlen = int((cu[1:] - cu[:-1]).max()) if cu.numel() > 1 else 0
+        desc = SeqDesc(_lib.THD, cu_seqlens.numel() - 1, T, int(max_seqlen), _ptr(cu_seqlens), hq, hkv, HEAD_DIM)
+        lead = (T,)
+    if out is None:
+        out = (torch.empty(lead + (hq, HEAD_DIM), dtype=torch.bfloat16, device=x.device),
+               torch.empty(lead + (hkv, HEAD_DIM), dtype=torch.bfloat16, device=x.device),
+               torch.empty(lead + (hkv, HEAD_DIM), dtype=torch.bfloat16, device=x.device))
+    q, k, v = out
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    check("gptoss_qkv_proj_rope", _lib.load().gptoss_qkv_proj_rope(
+        ctypes.byref(desc), _ptr(x), x.stride(-2), hidden, _ptr(wq), _ptr(bq), _ptr(wk), _ptr(bk), _ptr(wv),
+        _ptr(bv), tptr, trows, tdim, _ptr(q), _ptr(k), _ptr(v), _stream()))
+    return q, k, v

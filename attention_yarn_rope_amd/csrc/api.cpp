@@ -708,6 +708,61 @@ gptoss_status gptoss_attn_decode_kv(const gptoss_kv_layout* layout, int32_t num_
   return decode_run(p, num_q_heads, keys, keys, workspace, workspace_bytes, num_splits, stream);
 }
 
+gptoss_status gptoss_qkv_proj_rope(const gptoss_seq_desc* desc, const void* x, int64_t x_row_stride,
+                                   int32_t hidden, const void* wq, const void* bq, const void* wk, const void* bk,
+                                   const void* wv, const void* bv, const void* table, int32_t table_rows,
+                                   int32_t rotary_dim, void* q_out, void* k_out, void* v_out, void* stream) {
+  gptoss_status st = check_desc(desc);
+  if (st != GPTOSS_OK) return st;
+  if (hidden < 64 || hidden % 64 != 0)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 64", hidden);
+  if (desc->num_kv_heads % 4 != 0)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "num_kv_heads %d must be a multiple of 4", desc->num_kv_heads);
+  const int64_t T = desc_tokens(desc);
+  if (T == 0) return GPTOSS_OK;
+  if (!x || !wq || !wk || !wv || !q_out || !k_out || !v_out)
+    return fail(GPTOSS_ERR_NULL, "x, the weights and the outputs are required");
+  if (x_row_stride < hidden || (x_row_stride & 7) || !aligned16(x) || !aligned16(wq) || !aligned16(wk) ||
+      !aligned16(wv) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned, x_row_stride >= hidden and a multiple of 8");
+  for (const void* b : {bq, bk, bv})
+    if (reinterpret_cast<uintptr_t>(b) & 1) return fail(GPTOSS_ERR_UNSUPPORTED, "biases must be 2-byte aligned");
+  if ((int64_t)kProjTile * x_row_stride * 2 > (int64_t)INT32_MAX ||
+      (int64_t)kProjTile * hidden * 2 > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "one tile's rows of x or W must span less than 2 GiB");
+  if (table) {
+    if (rotary_dim != 64 && rotary_dim != 32)
+      return fail(GPTOSS_ERR_UNSUPPORTED, "rotary_dim %d: the projection epilogue rotates 64 or 32 dims", rotary_dim);
+    if (!aligned16(table)) return fail(GPTOSS_ERR_UNSUPPORTED, "table must be 16-byte aligned");
+    if (table_rows < std::max(desc_max_len(desc), 1))
+      return fail(GPTOSS_ERR_SHAPE, "table has %d rows, positions up to %d are needed", table_rows,
+                  desc_max_len(desc) - 1);
+  }
+  ProjParams p;
+  memset(&p, 0, sizeof p);
+  p.x = static_cast<const uint16_t*>(x);
+  p.x_st = x_row_stride;
+  p.w[0] = static_cast<const uint16_t*>(wq); p.w[1] = static_cast<const uint16_t*>(wk);
+  p.w[2] = static_cast<const uint16_t*>(wv);
+  p.b[0] = static_cast<const uint16_t*>(bq); p.b[1] = static_cast<const uint16_t*>(bk);
+  p.b[2] = static_cast<const uint16_t*>(bv);
+  p.out[0] = static_cast<uint16_t*>(q_out); p.out[1] = static_cast<uint16_t*>(k_out);
+  p.out[2] = static_cast<uint16_t*>(v_out);
+  p.nq = desc->num_q_heads * kHeadDim;
+  p.nkv = desc->num_kv_heads * kHeadDim;
+  p.tokens = (int32_t)T;
+  p.hidden = hidden;
+  p.m_tiles = (int32_t)((T + kProjTile - 1) / kProjTile);
+  p.n_tiles = (p.nq + 2 * p.nkv) / kProjTile;
+  p.batch = desc->batch;
+  p.seqlen = desc->seqlen;
+  p.cu_seqlens = desc->layout == GPTOSS_THD ? desc->cu_seqlens : nullptr;
+  p.table = static_cast<const uint16_t*>(table);
+  p.table_rows = table_rows;
+  p.rot_half = rotary_dim / 2;
+  return hip_status(launch_qkv_proj(p, static_cast<hipStream_t>(stream)), "projection kernel");
+}
+
 gptoss_status gptoss_kv_append(const gptoss_kv_layout* layout, void* k_cache, void* v_cache, int32_t num_seqs,
                                int32_t num_kv_heads, int32_t head_dim, int32_t num_new, const void* k_new,
                                const int64_t kn_strides[3], const void* v_new, const int64_t vn_strides[3],

@@ -72,6 +72,17 @@ __device__ __forceinline__ bool maybe_inexact_tie(float s, float p, float t) {
          (__builtin_fminf(__builtin_fabsf(p), __builtin_fabsf(t)) < __builtin_fabsf(s) * 0x1p-8f);
 }
 
+// Rotate one pair of bf16 values (held in floats) by a bf16 cos / sin: the
+// results RN(x1*C - x2*S) and RN(x2*C + x1*S), each rounded once to bf16 (the
+// products are exact in fp32; fix_bf16_tie repairs an inexact sum that lands on
+// a bf16 midpoint, branch free). Returns the two results as floats ready for
+// pack_bf16x2.
+__device__ __forceinline__ void rope1(float a1, float a2, float cc, float ss, float& o1, float& o2) {
+  const float p1 = a1 * cc, t1 = a2 * ss, p2 = a2 * cc, t2 = a1 * ss;
+  o1 = fix_bf16_tie(p1, -t1, p1 - t1);
+  o2 = fix_bf16_tie(p2, t2, p2 + t2);
+}
+
 // Rotate 8 pairs: x1 holds dims i..i+7, x2 their partners i+h..i+h+7 (h =
 // rotary_dim / 2), c / s the table's cos / sin for the same i. Writes rounded
 // bf16 outputs.
@@ -176,6 +187,16 @@ __device__ __forceinline__ uint4 ldb16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(bf16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Sequence index of packed token t: the largest n with cu[n] <= t.
+__device__ __forceinline__ int32_t find_seq(const int32_t* cu, int32_t num_seqs, int32_t t) {
+  int32_t lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    int32_t mid = (lo + hi + 1) >> 1;
+    if (__ldg(cu + mid) <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 // Rotation of one 64-dim row by a table row (cos of the rotary_dim / 2 pairs,
 // then their sin), for the 8-dim chunks c and c + 4 a thread owns. Chunk c <

@@ -128,6 +128,24 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 constexpr int kCacheContiguous = 0, kCachePaged = 1, kCacheRing = 2;   // gptoss_cache_kind
 
+// ---- q/k/v projection with the RoPE in its epilogue ----
+struct ProjParams {
+  const uint16_t* x; int64_t x_st;           // [tokens, hidden], row stride (elements)
+  const uint16_t* w[3];                      // q, k, v weights [out, hidden], rows contiguous
+  const uint16_t* b[3];                      // bf16 biases [out] (NULL: none)
+  uint16_t* out[3];                          // [tokens, out] contiguous
+  int32_t nq, nkv;                           // out widths: Hq * 64 and Hkv * 64
+  int32_t tokens, hidden;
+  int32_t m_tiles, n_tiles;
+  int32_t batch, seqlen;                     // positions: BSHD p = t mod seqlen; THD p = t - cu[n]
+  const int32_t* cu_seqlens;
+  const uint16_t* table;                     // NULL: no rotation
+  int32_t table_rows;
+  int32_t rot_half;                          // rotary_dim / 2 (16 or 32)
+};
+hipError_t launch_qkv_proj(const ProjParams& p, hipStream_t stream);
+constexpr int kProjTile = 256;   // tokens and output features per work group
+
 // ---- KV append ----
 struct AppendParams {
   uint16_t* k; uint16_t* v; int64_t c_s0, c_sr, c_sh;   // cache strides: sequence or page, row, head

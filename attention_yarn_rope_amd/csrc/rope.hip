@@ -42,15 +42,6 @@ __global__ void rope_table_kernel(TableParams p) {
   row[p.half + i] = f64_to_bf16(p.concentration * s);
 }
 
-// Sequence index of packed token t: the largest n with cu[n] <= t.
-__device__ __forceinline__ int32_t find_seq(const int32_t* cu, int32_t num_seqs, int32_t t) {
-  int32_t lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {
-    int32_t mid = (lo + hi + 1) >> 1;
-    if (__ldg(cu + mid) <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
 
 // One thread per (token row, head, chunk pair cc in 0..3).
 __global__ __launch_bounds__(256) void rope_qk_kernel(RopeQKParams p) {

@@ -167,6 +167,38 @@ def new_tokens(num_seqs, num_new, seed, hkv=HKV, d=HEAD_DIM):
     return _randn_bf16((num_seqs, num_new, hkv, d), g), _randn_bf16((num_seqs, num_new, hkv, d), g)
 
 
+@dataclass
+class Projection:
+    name: str
+    x: torch.Tensor                  # [tokens, hidden] bf16
+    wq: torch.Tensor                 # [Hq*64, hidden] bf16 (Linear weight layout)
+    bq: torch.Tensor                 # [Hq*64] bf16
+    wk: torch.Tensor
+    bk: torch.Tensor
+    wv: torch.Tensor
+    bv: torch.Tensor
+
+
+def projection(tokens, seed, hidden=2880, hq=HQ, hkv=HKV, d=HEAD_DIM, name=None):
+    """Inputs of the q/k/v projections (gpt-oss-20b print-out: hidden 2880, q 2880 -> 4096,
+    k / v 2880 -> 512, Linear with bias): x ~ N(0, 1); weights ~ N(0, 1 / hidden), the scale of
+    a Linear initialisation; biases ~ N(0, 0.1^2); all rounded to bf16. Draw order: x, wq, bq,
+    wk, bk, wv, bv."""
+    g = torch.Generator().manual_seed(seed)
+    x = _randn_bf16((tokens, hidden), g)
+    ws = []
+    for out in (hq * d, hkv * d, hkv * d):
+        w = (torch.randn((out, hidden), generator=g, dtype=torch.float32) * hidden ** -0.5).to(torch.bfloat16)
+        b = (torch.randn(out, generator=g, dtype=torch.float32) * 0.1).to(torch.bfloat16)
+        ws += [w, b]
+    return Projection(name or f"proj_T{tokens}", x, *ws)
+
+
+def projection_flops(tokens, hidden=2880, hq=HQ, hkv=HKV, d=HEAD_DIM):
+    """2 * hidden FLOPs per output element of x W^T (the bias adds and the rotation are not counted)."""
+    return 2 * tokens * hidden * (hq + 2 * hkv) * d
+
+
 def grad_out(shape, seed):
     """Gradient of the loss with respect to the attention output for the
     backward pass: torch.randn(shape) rounded to bfloat16, its own generator."""

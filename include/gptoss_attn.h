@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GPTOSS_ABI_VERSION 3
+#define GPTOSS_ABI_VERSION 4
 
 typedef enum {
   GPTOSS_OK = 0,
@@ -395,6 +395,34 @@ gptoss_status gptoss_attn_decode_kv(const gptoss_kv_layout* layout, int32_t num_
                                     void* out, const int64_t o_strides[2],
                                     void* workspace, size_t workspace_bytes, int32_t num_splits,
                                     void* stream);
+
+/*
+ * The q, k and v projections ahead of the attention with the RoPE applied to q
+ * and k in the same kernel (the gpt-oss-20b module print-out: q_proj
+ * 2880 -> Hq*64, k_proj and v_proj 2880 -> Hkv*64, Linear with bias; rope_utils
+ * page, _apply_rotary_emb_qk). Each output is z = x W^T + b accumulated in
+ * fp32 and rounded once to bf16, the projection's dtype; with a table, q and k
+ * are then rotated at each token's position exactly as gptoss_rope_qk rotates
+ * them, so the result equals gptoss_rope_qk applied to the table = NULL output,
+ * bit for bit.
+ *   desc:  token layout and positions (BSHD p = s, THD p = t - cu[n]); its
+ *          num_q_heads / num_kv_heads / head_dim give the output widths.
+ *   x:     device bf16 [tokens, hidden], rows x_row_stride elements apart.
+ *   wq [Hq*64, hidden], wk and wv [Hkv*64, hidden]: device bf16, Linear's
+ *          weight layout, rows contiguous.
+ *   bq, bk, bv: device bf16 biases of the same widths; NULL = no bias.
+ *   q_out [tokens, Hq, 64], k_out and v_out [tokens, Hkv, 64]: contiguous bf16.
+ *   table: NULL = no rotation; else rotary_dim 64 or 32 (the dims past it
+ *          pass through), table_rows >= the longest sequence.
+ * hidden must be a multiple of 64 and num_kv_heads a multiple of 4 (the q, k
+ * and v widths are multiples of the kernel's 256-feature tiles); other values
+ * return GPTOSS_ERR_UNSUPPORTED, as do unaligned pointers or strides.
+ */
+gptoss_status gptoss_qkv_proj_rope(const gptoss_seq_desc* desc, const void* x, int64_t x_row_stride,
+                                   int32_t hidden, const void* wq, const void* bq, const void* wk,
+                                   const void* bk, const void* wv, const void* bv, const void* table,
+                                   int32_t table_rows, int32_t rotary_dim, void* q_out, void* k_out,
+                                   void* v_out, void* stream);
 
 #ifdef __cplusplus
 }

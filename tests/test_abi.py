@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.gptoss_abi_version() == 3
+    assert lib.gptoss_abi_version() == 4
     for code in range(6):
         assert lib.gptoss_status_string(code)
     assert lib.gptoss_status_string(99) == b"unknown status"
@@ -317,3 +317,25 @@ def test_decode_kv_workspace_size(lib):
     assert lib.gptoss_attn_decode_kv_workspace_size(ctypes.byref(paged), 64, 64, 32768, 128, 0) == \
         lib.gptoss_attn_decode_workspace_size(64, 64, 159, 0)
     assert lib.gptoss_attn_decode_kv_workspace_size(None, 64, 64, 32768, 0, 0) == 0
+
+
+def _proj(lib, desc, **kw):
+    a = dict(x=P, xs=2880, hidden=2880, wq=P, bq=P, wk=P, bk=P, wv=P, bv=P, table=P, rows=4096, rd=64, q=P, k=P,
+             v=P)
+    a.update(kw)
+    return lib.gptoss_qkv_proj_rope(ctypes.byref(desc) if desc is not None else None, a["x"], a["xs"], a["hidden"],
+                                    a["wq"], a["bq"], a["wk"], a["bk"], a["wv"], a["bv"], a["table"], a["rows"],
+                                    a["rd"], a["q"], a["k"], a["v"], None)
+
+
+def test_projection_argument_errors(lib):
+    d = _desc_bshd()
+    assert _proj(lib, None) == ERR_NULL
+    assert _proj(lib, d, hidden=100) == ERR_UNSUPPORTED                     # not a multiple of 64
+    assert _proj(lib, SeqDesc(0, 2, 128, 128, None, 16, 2, 64)) == ERR_UNSUPPORTED   # Hkv not a multiple of 4
+    assert _proj(lib, d, wk=None) == ERR_NULL
+    assert _proj(lib, d, xs=2000) == ERR_UNSUPPORTED                        # row stride below hidden
+    assert _proj(lib, d, bq=ctypes.c_void_p(0x10001)) == ERR_UNSUPPORTED
+    assert _proj(lib, d, rd=48) == ERR_UNSUPPORTED                          # epilogue rotates 64 or 32 dims
+    assert _proj(lib, d, rows=100) == ERR_SHAPE                             # table shorter than the sequence
+    assert _proj(lib, SeqDesc(0, 0, 128, 128, None, 64, 8, 64)) == OK       # no tokens
