@@ -79,8 +79,14 @@ __device__ __forceinline__ bool maybe_inexact_tie(float s, float p, float t) {
 // pack_bf16x2.
 __device__ __forceinline__ void rope1(float a1, float a2, float cc, float ss, float& o1, float& o2) {
   const float p1 = a1 * cc, t1 = a2 * ss, p2 = a2 * cc, t2 = a1 * ss;
-  o1 = fix_bf16_tie(p1, -t1, p1 - t1);
-  o2 = fix_bf16_tie(p2, t2, p2 + t2);
+  o1 = p1 - t1;
+  o2 = p2 + t2;
+  // only a result on a bf16 midpoint can need the repair (rare: the lanes that do
+  // take the branch)
+  if (((__float_as_uint(o1) & 0xFFFFu) == 0x8000u) | ((__float_as_uint(o2) & 0xFFFFu) == 0x8000u)) {
+    o1 = fix_bf16_tie(p1, -t1, o1);
+    o2 = fix_bf16_tie(p2, t2, o2);
+  }
 }
 
 // Rotate 8 pairs: x1 holds dims i..i+7, x2 their partners i+h..i+h+7 (h =

@@ -18,11 +18,14 @@ synchronisation. The CPU baseline is the fp64 oracle on a time-bounded sample
 of query rows of the same workload, on this host's cores.
 
 The backward pass of both layers (dq, dk, dv, dsinks) is timed after the step and
-reported under "backward" (not part of `value`).
+reported under "backward" (not part of `value`). The q/k/v projections of the
+same tokens (hidden 2880, Linear with bias) with the RoPE in their epilogue are
+timed under "projection", next to torch's linear (hipBLASLt) followed by the
+standalone rotation, as context.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
        python bench.py --profile {prefill-full,prefill-window,decode-full,copy,backward-full,backward-window,
-                                  decode-paged,decode-ring,kv-append} --steps K
+                                  decode-paged,decode-ring,kv-append,proj-rope,proj} --steps K
        (the --profile modes run only the named call, for rocprofv3)
 """
 
@@ -224,7 +227,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy",
                                                         "backward-full", "backward-window", "decode-paged",
-                                                        "decode-ring", "kv-append"])
+                                                        "decode-ring", "kv-append", "proj-rope", "proj"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -279,6 +282,33 @@ def main():
         log(f"{args.profile}: {args.steps} launches")
         return
 
+    # ---------------- q/k/v projections with the RoPE in the epilogue ----------------
+    def projection_calls():
+        pw = wl.projection(q.shape[0] * S, seed=50)
+        px = pw.x.to(dev).reshape(q.shape[0], S, -1)
+        wts = [t.to(dev) for t in (pw.wq, pw.bq, pw.wk, pw.bk, pw.wv, pw.bv)]
+        outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        wcat = torch.cat([wts[0], wts[2], wts[4]]).contiguous()
+        bcat = torch.cat([wts[1], wts[3], wts[5]]).contiguous()
+        nq, nk = q.shape[2] * 64, k.shape[2] * 64
+
+        def torch_path():
+            y = torch.nn.functional.linear(px, wcat, bcat)
+            return gx.rope_qk(y[..., :nq].reshape(q.shape), y[..., nq:nq + nk].reshape(k.shape), table)
+
+        return {"fused": lambda: gx.qkv_proj_rope(px, *wts, table=table, out=outs),
+                "unrotated": lambda: gx.qkv_proj_rope(px, *wts, out=outs),
+                "torch_linear_rope_qk": torch_path,
+                "flops": wl.projection_flops(q.shape[0] * S, hidden=px.shape[-1])}
+
+    if args.profile in ("proj-rope", "proj"):
+        fn = projection_calls()["fused" if args.profile == "proj-rope" else "unrotated"]
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"{args.profile}: {args.steps} calls")
+        return
+
     # ---------------- backward of both layers (measured beside the step) ----------------
     def backward_calls():
         """One forward with lse per layer, then closures that run each layer's backward."""
@@ -325,6 +355,35 @@ def main():
         log(f"[bench] prefill step {ms_step:.3f} ms (full {ms_full:.3f} ms, window {ms_win:.3f} ms, "
             f"table {ms_table:.4f} ms)")
         del timer
+
+    projection_obj = None
+    if args.profile is None:
+        pc = projection_calls()
+        timer = Timer(torch)
+        names = ("fused", "unrotated", "torch_linear_rope_qk")
+        for _ in range(args.warmup):
+            for n in names:
+                pc[n]()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            for n in names:
+                timer.run(n, pc[n])
+        torch.cuda.synchronize()
+        pfl = pc["flops"]
+        projection_obj = {
+            "workload": f"q/k/v projections of the dense prefill's {q.shape[0] * S} tokens: hidden 2880 -> "
+                        "4096 / 512 / 512, Linear with bias, bf16; q and k rotated with the table in the epilogue",
+            "flops": pfl,
+        }
+        for n in names:
+            ms = timer.mean_ms(n)
+            projection_obj[n] = {"ms": round(ms, 4), "TFLOP/s": round(pfl / (ms * 1e-3) / 1e12, 1),
+                                 "frac_mfma_peak": round(pfl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        projection_obj["torch_linear_rope_qk"]["note"] = "context: torch.nn.functional.linear (hipBLASLt) then " \
+                                                         "gptoss_rope_qk"
+        log(f"[bench] projection fused {projection_obj['fused']['ms']:.3f} ms "
+            f"({projection_obj['fused']['TFLOP/s']:.0f} TFLOP/s)")
+        del pc, timer
 
     backward_obj = None
     if args.profile is None and not args.no_backward:
@@ -453,6 +512,7 @@ def main():
             "table_ms": round(ms_table, 5),
         },
         "backward": backward_obj,
+        "projection": projection_obj,
         "decode": decode_obj,
         "cpu_baseline": None,
     }
