@@ -1,5 +1,6 @@
 """GPT-OSS attention hot path on MI355X: YaRN RoPE, sink + GQA + sliding-window
-prefill (BSHD and packed THD) with its backward pass, split-KV decode over
+prefill (BSHD and packed THD) with its backward pass and its context-parallel
+shard + merge form, split-KV decode over
 contiguous, paged or ring KV caches, the cache append, and the q/k/v
 projections with the RoPE in their epilogue, as
 hand-written gfx950 HIP kernels behind a C ABI (include/gptoss_attn.h). This
@@ -17,6 +18,8 @@ from .api import (  # noqa: F401
     attn_prefill_backward,
     attn_decode,
     qkv_proj_rope,
+    attn_prefill_shard,
+    attn_merge,
     kv_layout,
     kv_append,
     attn_decode_kv,

@@ -63,6 +63,12 @@ SIGNATURES = {
                                                     c_vp, I64x3, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                     c_vp, c_size, c_vp]),
     "gptoss_attn_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "gptoss_attn_prefill_shard_workspace_size": (c_size, [ctypes.POINTER(SeqDesc), c_i32]),
+    "gptoss_attn_prefill_shard": (ctypes.c_int, [ctypes.POINTER(SeqDesc), c_vp, I64x3, c_vp, I64x3, c_vp, I64x3,
+                                                 c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_i32, c_i32, c_vp,
+                                                 I64x3, c_vp, c_vp, c_size, c_vp]),
+    "gptoss_attn_merge": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, c_i64 * 4, c_vp, c_vp, c_vp, I64x2,
+                                         c_vp, c_vp]),
     "gptoss_qkv_proj_rope": (ctypes.c_int, [ctypes.POINTER(SeqDesc), c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp,
                                             c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "gptoss_kv_append": (ctypes.c_int, [ctypes.POINTER(KVLayout), c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, I64x3,

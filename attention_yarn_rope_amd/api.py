@@ -374,3 +374,45 @@ def qkv_proj_rope(x, wq, bq, wk, bk, wv, bv, table=None, cu_seqlens=None, max_se
         ctypes.byref(desc), _ptr(x), x.stride(-2), hidden, _ptr(wq), _ptr(bq), _ptr(wk), _ptr(bk), _ptr(wv),
         _ptr(bv), tptr, trows, tdim, _ptr(q), _ptr(k), _ptr(v), _stream()))
     return q, k, v
+
+
+def attn_prefill_shard(q, k, v, q_offset, kv_offset, window=0, table=None, softmax_scale=None, out=None, lse=None,
+                       workspace=None):
+    """One step of a context-parallel prefill: q [B, Sq, Hq, D] at positions q_offset + s against
+    k, v [B, Sk, Hkv, D] at kv_offset + j, no sink. Returns (out, lse [B * Sq, Hq])."""
+    _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v")
+    if q.dim() != 4:
+        raise ValueError("shards are BSHD: q [B, S, Hq, D]")
+    B, S, Hq, D = q.shape
+    desc = SeqDesc(_lib.BSHD, B, S, S, None, Hq, k.shape[2], D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B * S, Hq), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    if workspace is None:
+        need = lib.gptoss_attn_prefill_shard_workspace_size(ctypes.byref(desc), k.shape[1])
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    check("gptoss_attn_prefill_shard", lib.gptoss_attn_prefill_shard(
+        ctypes.byref(desc), _ptr(q), _strides3(q, _lib.BSHD), _ptr(k), _strides3(k, _lib.BSHD), _ptr(v),
+        _strides3(v, _lib.BSHD), k.shape[1], int(q_offset), int(kv_offset), float(scale), int(window), tptr, trows,
+        tdim, _ptr(out), _strides3(out, _lib.BSHD), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
+
+
+def attn_merge(o_parts, lse_parts, sinks=None, out=None, lse_out=None):
+    """Merge partial results: o_parts [P, T, Hq, D] bf16, lse_parts [P, T * Hq] fp32 -> out [T, Hq, D]
+    (and lse [T * Hq] when lse_out is given); the sink is added once."""
+    _bf16(o_parts, "o_parts")
+    P, T, Hq, D = o_parts.shape
+    if lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous() or lse_parts.numel() != P * T * Hq:
+        raise ValueError("lse_parts must be a contiguous float32 [P, T * Hq] tensor")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=o_parts.device)
+    ps = o_parts.stride()
+    check("gptoss_attn_merge", _lib.load().gptoss_attn_merge(
+        P, T, Hq, D, _ptr(o_parts), (ctypes.c_int64 * 4)(ps[0], ps[1], ps[2], ps[3]), _ptr(lse_parts),
+        _ptr(sinks), _ptr(out), I64x2(out.stride(0), out.stride(1)), _ptr(lse_out), _stream()))
+    return out

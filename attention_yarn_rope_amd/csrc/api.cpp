@@ -204,6 +204,7 @@ gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc, const void* q, const i
     p.table = static_cast<const uint16_t*>(table);
     p.table_rows = table_rows;
     p.rot_chunks = rotary_dim / 16;
+    p.pos0 = 0;
     if (thd && desc->batch == 0) return GPTOSS_OK;
     st = hip_status(launch_rope_qk(p, s), "rope_qk kernel");
     if (st != GPTOSS_OK) return st;
@@ -211,28 +212,32 @@ gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc, const void* q, const i
   return GPTOSS_OK;
 }
 
-size_t gptoss_attn_prefill_workspace_size(const gptoss_seq_desc* desc) {
-  if (check_desc(desc) != GPTOSS_OK) return 0;
-  size_t bytes = 0;
-  if (desc->layout == GPTOSS_THD) bytes += round_up((size_t)thd_max_items(desc) * sizeof(int2)) + kAlign;
-  // rotated K when k is rotated by a separate pass
-  bytes += round_up((size_t)desc_tokens(desc) * desc->num_kv_heads * kHeadDim * sizeof(uint16_t));
-  return bytes;
-}
-
 }  // extern "C"
 
 namespace {
+// A BSHD query shard against a key shard of a longer sequence (NULL: whole sequences).
+struct ShardArgs {
+  int32_t kv_len, q_offset, kv_offset;
+};
+
+size_t prefill_ws_bytes(const gptoss_seq_desc* desc, int64_t kv_tokens) {
+  size_t bytes = 0;
+  if (desc->layout == GPTOSS_THD) bytes += round_up((size_t)thd_max_items(desc) * sizeof(int2)) + kAlign;
+  // rotated K when k is rotated by a separate pass
+  bytes += round_up((size_t)kv_tokens * desc->num_kv_heads * kHeadDim * sizeof(uint16_t));
+  return bytes;
+}
+
 gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
                            const void* k, const int64_t k_strides[3], const void* v,
                            const int64_t v_strides[3], const float* sinks, float softmax_scale,
                            int32_t window, const void* table, int32_t table_rows, int32_t rotary_dim,
                            void* out, const int64_t o_strides[3], float* lse, void* workspace,
-                           size_t workspace_bytes, int krot, void* stream) {
+                           size_t workspace_bytes, int krot, void* stream, const ShardArgs* shard = nullptr) {
   gptoss_status st = check_desc(desc);
   if (st != GPTOSS_OK) return st;
   if (desc_tokens(desc) == 0 || desc->batch == 0) return GPTOSS_OK;
-  if (!q || !k || !v || !out || !sinks || !q_strides || !k_strides || !v_strides || !o_strides)
+  if (!q || !k || !v || !out || (!sinks && !shard) || !q_strides || !k_strides || !v_strides || !o_strides)
     return fail(GPTOSS_ERR_NULL, "q, k, v, out, sinks and all strides are required");
   if (!strides_ok(q_strides, 3) || !strides_ok(k_strides, 3) || !strides_ok(v_strides, 3) ||
       !strides_ok(o_strides, 3) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -243,9 +248,13 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
   // a 64-key tile of K or V must span less than 2 GiB (32-bit buffer offsets)
   if (k_strides[1] * 2 * 64 > (int64_t)INT32_MAX || v_strides[1] * 2 * 64 > (int64_t)INT32_MAX)
     return fail(GPTOSS_ERR_UNSUPPORTED, "token strides of k and v must be below 2^24 elements");
-  st = check_table(table, table_rows, rotary_dim, desc_max_len(desc));
+  // rows of the table the rotations read
+  const int32_t need_rows = shard ? std::max(shard->q_offset + desc->seqlen, shard->kv_offset + shard->kv_len)
+                                  : desc_max_len(desc);
+  st = check_table(table, table_rows, rotary_dim, need_rows);
   if (st != GPTOSS_OK) return st;
-  const size_t need = gptoss_attn_prefill_workspace_size(desc);
+  const int32_t kv_len = shard ? shard->kv_len : desc->seqlen;   // BSHD keys per sequence
+  const size_t need = prefill_ws_bytes(desc, shard ? (int64_t)desc->batch * kv_len : desc_tokens(desc));
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
     return fail(GPTOSS_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                 workspace_bytes);
@@ -264,7 +273,9 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
   p.v_sb = thd ? 0 : v_strides[0]; p.v_st = v_strides[1]; p.v_sh = v_strides[2];
   p.o = static_cast<uint16_t*>(out);
   p.o_sb = thd ? 0 : o_strides[0]; p.o_st = o_strides[1]; p.o_sh = o_strides[2];
-  p.sinks = sinks;
+  // without sinks the kernel still loads Hq floats, from q (any readable memory; the values are ignored)
+  p.sinks = sinks ? sinks : static_cast<const float*>(q);
+  p.no_sink = sinks ? 0 : 1;
   p.table = static_cast<const uint16_t*>(table);
   p.table_rows = table_rows;
   p.batch = desc->batch;
@@ -274,6 +285,12 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
   p.lse = lse;
+  p.kv_len = kv_len;
+  if (shard) {
+    p.q_shift = shard->q_offset - shard->kv_offset;
+    p.q_pos0 = shard->q_offset;
+    p.k_pos0 = shard->kv_offset;
+  }
 
   if (thd) {
     const int32_t max_items = thd_max_items(desc);
@@ -299,19 +316,20 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
     r.s_b = p.k_sb; r.s_t = p.k_st; r.s_h = p.k_sh;
     r.y = krot_buf;
     r.batch = thd ? 1 : desc->batch;
-    r.tokens = desc->seqlen;
+    r.tokens = thd ? desc->seqlen : kv_len;
     r.heads = desc->num_kv_heads;
     r.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
     r.num_seqs = desc->batch;
     r.table = p.table;
     r.table_rows = table_rows;
     r.rot_chunks = kHeadDim / 16;
+    r.pos0 = p.k_pos0;
     st = hip_status(launch_rope_qk(r, s), "k rotation kernel");
     if (st != GPTOSS_OK) return st;
     p.k = krot_buf;
     p.k_sh = kHeadDim;
     p.k_st = (int64_t)desc->num_kv_heads * kHeadDim;
-    p.k_sb = thd ? 0 : (int64_t)desc->seqlen * p.k_st;
+    p.k_sb = thd ? 0 : (int64_t)kv_len * p.k_st;
   }
   return hip_status(launch_prefill(p, thd, krot, s), "prefill kernel");
 }
@@ -361,6 +379,70 @@ gptoss_status gptoss_attn_prefill_ex(const gptoss_seq_desc* desc, const void* q,
   }
   return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, sinks, softmax_scale, window, table,
                       table_rows, rotary_dim, out, o_strides, nullptr, workspace, workspace_bytes, krot, stream);
+}
+
+size_t gptoss_attn_prefill_workspace_size(const gptoss_seq_desc* desc) {
+  if (check_desc(desc) != GPTOSS_OK) return 0;
+  return prefill_ws_bytes(desc, desc_tokens(desc));
+}
+
+size_t gptoss_attn_prefill_shard_workspace_size(const gptoss_seq_desc* desc, int32_t kv_len) {
+  if (check_desc(desc) != GPTOSS_OK || desc->layout != GPTOSS_BSHD || kv_len < 0) return 0;
+  return prefill_ws_bytes(desc, (int64_t)desc->batch * kv_len);
+}
+
+gptoss_status gptoss_attn_prefill_shard(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
+                                        const void* k, const int64_t k_strides[3], const void* v,
+                                        const int64_t v_strides[3], int32_t kv_len, int32_t q_offset,
+                                        int32_t kv_offset, float softmax_scale, int32_t window, const void* table,
+                                        int32_t table_rows, int32_t rotary_dim, void* out,
+                                        const int64_t o_strides[3], float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  gptoss_status st = check_desc(desc);
+  if (st != GPTOSS_OK) return st;
+  if (desc->layout != GPTOSS_BSHD) return fail(GPTOSS_ERR_UNSUPPORTED, "shards are BSHD");
+  if (kv_len < 0 || q_offset < 0 || kv_offset < 0)
+    return fail(GPTOSS_ERR_SHAPE, "kv_len, q_offset and kv_offset must be >= 0");
+  if ((int64_t)q_offset + desc->seqlen > INT32_MAX || (int64_t)kv_offset + kv_len > INT32_MAX)
+    return fail(GPTOSS_ERR_SHAPE, "positions must stay below 2^31");
+  if (!lse) return fail(GPTOSS_ERR_NULL, "lse is required (the merge weights the shards by it)");
+  if (reinterpret_cast<uintptr_t>(lse) & 15) return fail(GPTOSS_ERR_UNSUPPORTED, "lse must be 16-byte aligned");
+  // no sink here (sinks = NULL: the shard's own softmax); the merge adds it once
+  const ShardArgs sh{kv_len, q_offset, kv_offset};
+  return prefill_impl(desc, q, q_strides, k, k_strides, v, v_strides, nullptr, softmax_scale,
+                      window, table, table_rows, rotary_dim, out, o_strides, lse, workspace, workspace_bytes,
+                      KROT_NONE, stream, &sh);
+}
+
+gptoss_status gptoss_attn_merge(int32_t num_parts, int32_t tokens, int32_t num_q_heads, int32_t head_dim,
+                                const void* o_parts, const int64_t part_strides[4], const float* lse_parts,
+                                const float* sinks, void* out, const int64_t o_strides[2], float* lse_out,
+                                void* stream) {
+  if (num_parts < 0 || tokens < 0 || num_q_heads < 1) return fail(GPTOSS_ERR_SHAPE, "negative size or no heads");
+  if (head_dim != kHeadDim) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", head_dim);
+  if (tokens == 0) return GPTOSS_OK;
+  if (!out || !o_strides || (num_parts > 0 && (!o_parts || !part_strides || !lse_parts)))
+    return fail(GPTOSS_ERR_NULL, "out, its strides and (with parts) the parts, their strides and lse are required");
+  if (num_parts > 0 && (part_strides[0] < 0 || part_strides[1] < 0 || part_strides[2] < 0 || part_strides[3] != 1 ||
+                        (reinterpret_cast<uintptr_t>(o_parts) & 1)))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "part strides must be non-negative with the head dim contiguous");
+  if (o_strides[0] < 0 || o_strides[1] < 0 || (o_strides[0] & 1) || (o_strides[1] & 1) ||
+      (reinterpret_cast<uintptr_t>(out) & 3))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "out must be 4-byte aligned with even strides");
+  MergeParams p;
+  memset(&p, 0, sizeof p);
+  p.o = static_cast<const uint16_t*>(o_parts);
+  if (num_parts > 0) { p.o_sp = part_strides[0]; p.o_st = part_strides[1]; p.o_sh = part_strides[2]; }
+  p.lse = lse_parts;
+  p.l_sp = (int64_t)tokens * num_q_heads;
+  p.sinks = sinks;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_st = o_strides[0]; p.out_sh = o_strides[1];
+  p.lse_out = lse_out;
+  p.parts = num_parts;
+  p.tokens = tokens;
+  p.num_q_heads = num_q_heads;
+  return hip_status(launch_merge(p, static_cast<hipStream_t>(stream)), "merge kernel");
 }
 
 // ---------------------------------------------------------------------------

@@ -83,7 +83,8 @@ __device__ __forceinline__ void rope1(float a1, float a2, float cc, float ss, fl
   o2 = p2 + t2;
   // only a result on a bf16 midpoint can need the repair (rare: the lanes that do
   // take the branch)
-  if (((__float_as_uint(o1) & 0xFFFFu) == 0x8000u) | ((__float_as_uint(o2) & 0xFFFFu) == 0x8000u)) {
+  const uint32_t mid = ((__float_as_uint(o1) & 0xFFFFu) ^ 0x8000u) * ((__float_as_uint(o2) & 0xFFFFu) ^ 0x8000u);
+  if (mid == 0u) {
     o1 = fix_bf16_tie(p1, -t1, o1);
     o2 = fix_bf16_tie(p2, t2, o2);
   }

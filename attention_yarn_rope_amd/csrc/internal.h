@@ -31,6 +31,7 @@ struct RopeQKParams {
   const uint16_t* table;         // [table_rows, rotary_dim]: cos of the rotary_dim / 2 pairs, then sin
   int32_t table_rows;
   int32_t rot_chunks;            // rotary_dim / 16: 8-dim chunks in each half of the rotated part
+  int32_t pos0;                  // BSHD: token s is at position pos0 + s (a shard of a longer sequence)
 };
 hipError_t launch_rope_qk(const RopeQKParams& p, hipStream_t stream);
 
@@ -40,7 +41,8 @@ struct PrefillParams {
   const uint16_t* k; int64_t k_sb, k_st, k_sh;
   const uint16_t* v; int64_t v_sb, v_st, v_sh;
   uint16_t* o; int64_t o_sb, o_st, o_sh;
-  const float* sinks;
+  const float* sinks;            // always a readable [Hq] array (see no_sink)
+  int32_t no_sink;               // 1: no sink term (the sinks are loaded and ignored)
   const uint16_t* table;         // NULL: q (and k) already rotated
   int32_t table_rows;
   int32_t batch;                 // BSHD batch, or number of THD sequences
@@ -53,6 +55,12 @@ struct PrefillParams {
   const int2* work;              // THD work list (seq, q block), longest first
   const int32_t* work_count;     // THD: number of valid entries in `work`
   float* lse;                    // optional fp32 [tokens, num_q_heads] log-sum-exp per row (NULL: none)
+  // BSHD shards of a longer sequence (whole sequences: 0, seqlen, 0, 0): query s
+  // sits at position s + q_shift of the keys' coordinates; kv_len keys per
+  // sequence; q and k rotated with table rows offset by q_pos0 and k_pos0
+  int32_t q_shift;
+  int32_t kv_len;
+  int32_t q_pos0, k_pos0;
 };
 enum KRotation { KROT_NONE = 0, KROT_FUSED = 1 };
 hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_t stream);
@@ -144,6 +152,17 @@ struct ProjParams {
   int32_t rot_half;                          // rotary_dim / 2 (16 or 32)
 };
 hipError_t launch_qkv_proj(const ProjParams& p, hipStream_t stream);
+
+// ---- merge of partial attention outputs (shards of the keys) ----
+struct MergeParams {
+  const uint16_t* o; int64_t o_sp, o_st, o_sh;   // bf16 partial outputs [parts, tokens, Hq, 64]
+  const float* lse; int64_t l_sp;                // fp32 [parts, tokens * Hq]: natural log, -inf = no keys
+  const float* sinks;                            // [Hq], -inf allowed
+  uint16_t* out; int64_t out_st, out_sh;         // bf16 [tokens, Hq, 64]
+  float* lse_out;                                // optional [tokens * Hq]
+  int32_t parts, tokens, num_q_heads;
+};
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 constexpr int kProjTile = 256;   // tokens and output features per work group
 
 // ---- KV append ----

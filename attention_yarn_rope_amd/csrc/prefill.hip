@@ -27,6 +27,8 @@
 // the hot loop has no running max and no accumulator rescale. Tiles fully
 // visible to every query of the item skip the mask; tiles fully hidden are
 // never visited.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -120,8 +122,13 @@ void prefill_kernel(PrefillParams p) {
   const int qlast = min(q0 + BQ, L) - 1;
   const int W = p.window;
   const uint32_t weff = (W > 0) ? (uint32_t)W : 0x7FFFFFFFu;   // keys visible: 0 <= qpos - kpos < weff
-  const int kv_lo = (W > 0) ? max(0, q0 - W + 1) : 0;
-  const int kv_hi = qlast + 1;
+  // Query positions in the keys' coordinates: a shard of a longer sequence has
+  // its queries q_shift positions after its first key (0 for a whole sequence)
+  // and its own key count.
+  const int qk0 = q0 + p.q_shift, qklast = qlast + p.q_shift;
+  const int Lk = THD ? L : p.kv_len;
+  const int kv_lo = (W > 0) ? max(0, qk0 - W + 1) : 0;
+  const int kv_hi = min(qklast + 1, Lk);
   const int ntiles = (kv_hi - kv_lo + NK - 1) / NK;
   const float sl = p.scale_log2;
 
@@ -148,7 +155,7 @@ void prefill_kernel(PrefillParams p) {
     if (SH::kChunks == 2) { st.k2 = ldb16(rk, koff + 64); st.v2 = ldb16(rv, voff + 64); }
     if (ROTK) {
       const int kpos = kv_lo + t * NK + srow;
-      const bf16_t* tp = p.table + (int64_t)min(min(kpos, kv_hi - 1), p.table_rows - 1) * kHeadDim + 8 * scc;
+      const bf16_t* tp = p.table + (int64_t)min(min(kpos, kv_hi - 1) + p.k_pos0, p.table_rows - 1) * kHeadDim + 8 * scc;
       st.c = ldg16(tp); st.s = ldg16(tp + 32);
     }
   };
@@ -178,9 +185,19 @@ void prefill_kernel(PrefillParams p) {
     load_tile(0, st[0]);
   }
   bf16x8_t qf[CB][2];
-  int qpos[2];
+  int qpos[2], qkp[2];   // query rows, and their positions in the keys' coordinates
   qpos[0] = q0 + col;
   qpos[1] = q0 + 16 + col;
+  qkp[0] = qpos[0] + p.q_shift;
+  qkp[1] = qpos[1] + p.q_shift;
+  int vbase[2];
+  uint32_t vlim[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int lo = max(0, qkp[c] - kv_hi + 1);
+    vbase[c] = qkp[c] - lo;
+    vlim[c] = (uint32_t)max((int)weff - lo, 0);
+  }
   uint4 qx[CB][2], qt[CB][2];
   float sink_raw[CB];
 #pragma unroll
@@ -191,7 +208,7 @@ void prefill_kernel(PrefillParams p) {
     qx[cb][0] = ldg16(qp + 8 * grp);
     qx[cb][1] = ldg16(qp + 32 + 8 * grp);
     if (ROTQ) {
-      const bf16_t* tp = p.table + (int64_t)min(pos, p.table_rows - 1) * kHeadDim + 8 * grp;
+      const bf16_t* tp = p.table + (int64_t)min(pos + p.q_pos0, p.table_rows - 1) * kHeadDim + 8 * grp;
       qt[cb][0] = ldg16(tp);
       qt[cb][1] = ldg16(tp + 32);
     }
@@ -206,7 +223,7 @@ void prefill_kernel(PrefillParams p) {
     qf[cb][1] = as_bf16x8(y2);
     // reference = the sink logit (log2 units); the sink term exp2(sigma - ref) = 1
     // is counted once, in lane group 0. A sink of -inf contributes 0 (reference 0).
-    const float sink = sink_raw[cb] * kLog2e;
+    const float sink = p.no_sink ? -INFINITY : sink_raw[cb] * kLog2e;   // no sink: a shard of the keys
     const bool has_sink = sink > -INFINITY;
     ref[cb] = has_sink ? sink : 0.0f;
     lsum[cb] = (grp == 0 && has_sink) ? 1.0f : 0.0f;
@@ -249,16 +266,20 @@ void prefill_kernel(PrefillParams p) {
     }
 
     // ---- mask: only steps that are not fully visible to every query of the item.
-    // visible <=> 0 <= qpos - kpos < weff, one unsigned compare (branch free) ----
-    const bool full = (tile0 + NKT - 1 <= q0) && (W == 0 || qlast - tile0 < W);
+    // visible <=> lo <= qpos - kpos < weff, one unsigned compare (branch free):
+    // (qpos - lo - kpos) < (weff - lo) with the column's vbase = qpos - lo and
+    // vlim = weff - lo. lo = 0 for a whole sequence; a shard of the keys can end
+    // before its queries, and then lo = qpos - kv_hi + 1 hides the rows past the
+    // keys (they read as zeros) ----
+    const bool full = (tile0 + NKT - 1 <= qk0) && (W == 0 || qklast - tile0 < W) && (tile0 + NKT <= kv_hi);
     if (!full) {
 #pragma unroll
       for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int kpos = tile0 + kb * 16 + 4 * grp + r;
-          const bool vis0 = (uint32_t)(qpos[0] - kpos) < weff;
-          const bool vis1 = (uint32_t)(qpos[1] - kpos) < weff;
+          const bool vis0 = (uint32_t)(vbase[0] - kpos) < vlim[0];
+          const bool vis1 = (uint32_t)(vbase[1] - kpos) < vlim[1];
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             const bool vis = (cb & 1) ? vis1 : vis0;

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(RopeQKParams p) {
   const int64_t bt = r / p.heads;
   const int32_t b = (int32_t)(bt / p.tokens);
   const int32_t t = (int32_t)(bt - (int64_t)b * p.tokens);
-  int32_t pos = t;
+  int32_t pos = t + p.pos0;
   if (p.cu_seqlens) pos = t - __ldg(p.cu_seqlens + find_seq(p.cu_seqlens, p.num_seqs, t));
   pos = min(max(pos, 0), p.table_rows - 1);
   const uint16_t* x = p.x + b * p.s_b + t * p.s_t + h * p.s_h;

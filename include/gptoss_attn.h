@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GPTOSS_ABI_VERSION 4
+#define GPTOSS_ABI_VERSION 5
 
 typedef enum {
   GPTOSS_OK = 0,
@@ -308,6 +308,53 @@ gptoss_status gptoss_attn_decode(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  void* out, const int64_t o_strides[2],
                                  void* workspace, size_t workspace_bytes, int32_t num_splits,
                                  void* stream);
+
+/*
+ * One step of a context-parallel prefill: a BSHD shard of queries against a
+ * shard of keys of the same sequences, without the sink (layers page,
+ * GptOssAttention; rope_utils page: rotations at global positions, the
+ * context-parallel arguments that split a sequence over ranks). Query s of
+ * the shard sits at position q_offset + s, key j at kv_offset + j; the causal
+ * / window mask and the rotations use those positions. Each row's result is
+ * the attention over the shard's visible keys alone:
+ *   lse = log sum_j e^{s_j} (natural log; -inf with no visible key),
+ *   out = sum_j e^{s_j - lse} v_j (0 with none),
+ * which gptoss_attn_merge combines across shards, adding the sink once.
+ *   desc:   BSHD, seqlen = the query shard's length (THD: UNSUPPORTED).
+ *   k, v:   [batch, kv_len, Hkv, 64] with k_strides / v_strides.
+ *   table:  rotates q at q_offset + s and k at kv_offset + j (NULL: both
+ *           pre-rotated); table_rows must cover both.
+ *   out:    bf16 like q; lse: fp32 [batch * seqlen, Hq], 16-byte aligned.
+ *   workspace: >= gptoss_attn_prefill_shard_workspace_size(desc, kv_len).
+ * Errors as for gptoss_attn_prefill.
+ */
+size_t gptoss_attn_prefill_shard_workspace_size(const gptoss_seq_desc* desc, int32_t kv_len);
+gptoss_status gptoss_attn_prefill_shard(const gptoss_seq_desc* desc,
+                                        const void* q, const int64_t q_strides[3],
+                                        const void* k, const int64_t k_strides[3],
+                                        const void* v, const int64_t v_strides[3],
+                                        int32_t kv_len, int32_t q_offset, int32_t kv_offset,
+                                        float softmax_scale, int32_t window,
+                                        const void* table, int32_t table_rows, int32_t rotary_dim,
+                                        void* out, const int64_t o_strides[3], float* lse,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge partial attention results over disjoint sets of keys (the shards of
+ * gptoss_attn_prefill_shard) and add the per-head sink once:
+ *   lse = log(e^sigma_h + sum_p e^{lse_p}),  out = sum_p e^{lse_p - lse} o_p.
+ *   o_parts:    bf16 [num_parts, tokens, Hq, 64], element strides part_strides
+ *               {part, token, head, 1}.
+ *   lse_parts:  fp32 [num_parts, tokens * Hq], contiguous (-inf: no keys).
+ *   sinks:      fp32 [Hq]; NULL = no sink.
+ *   out:        bf16 [tokens, Hq, 64] with o_strides {token, head} (even).
+ *   lse_out:    optional fp32 [tokens * Hq] (NULL: not written).
+ * num_parts = 0 gives out = 0 (lse_out = sigma).
+ */
+gptoss_status gptoss_attn_merge(int32_t num_parts, int32_t tokens, int32_t num_q_heads, int32_t head_dim,
+                                const void* o_parts, const int64_t part_strides[4], const float* lse_parts,
+                                const float* sinks, void* out, const int64_t o_strides[2], float* lse_out,
+                                void* stream);
 
 /* ---- KV caches of the decode loop ----
  * No page specifies a KV cache. The pages' generation loop (model.generate in

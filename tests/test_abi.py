@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.gptoss_abi_version() == 4
+    assert lib.gptoss_abi_version() == 5
     for code in range(6):
         assert lib.gptoss_status_string(code)
     assert lib.gptoss_status_string(99) == b"unknown status"
@@ -339,3 +339,27 @@ def test_projection_argument_errors(lib):
     assert _proj(lib, d, rd=48) == ERR_UNSUPPORTED                          # epilogue rotates 64 or 32 dims
     assert _proj(lib, d, rows=100) == ERR_SHAPE                             # table shorter than the sequence
     assert _proj(lib, SeqDesc(0, 0, 128, 128, None, 64, 8, 64)) == OK       # no tokens
+
+
+def test_shard_and_merge_argument_errors(lib):
+    d = _desc_bshd()
+    f = lib.gptoss_attn_prefill_shard
+    args = lambda **kw: dict(dict(q=P, k=P, v=P, kvl=128, qo=0, ko=0, lse=P, ws=P, wsb=1 << 30, rows=4096), **kw)
+    call = lambda desc, **kw: (lambda a: f(ctypes.byref(desc), a["q"], S3, a["k"], K3, a["v"], K3, a["kvl"], a["qo"],
+                                           a["ko"], 0.125, 0, P, a["rows"], 64, P, S3, a["lse"], a["ws"], a["wsb"],
+                                           None))(args(**kw))
+    assert call(SeqDesc(1, 2, 100, 50, P, 64, 8, 64)) == ERR_UNSUPPORTED     # THD
+    assert call(d, kvl=-1) == ERR_SHAPE
+    assert call(d, qo=-5) == ERR_SHAPE
+    assert call(d, lse=None) == ERR_NULL
+    assert call(d, lse=ctypes.c_void_p(0x10004)) == ERR_UNSUPPORTED
+    assert call(d, qo=4000, rows=4096) == ERR_SHAPE                          # table must cover q_offset + S
+    assert call(d, wsb=16) == ERR_WORKSPACE
+    assert lib.gptoss_attn_prefill_shard_workspace_size(ctypes.byref(d), 256) == 2 * 256 * 8 * 64 * 2
+    m = lib.gptoss_attn_merge
+    st4 = (ctypes.c_int64 * 4)(128 * 64 * 64, 64 * 64, 64, 1)
+    assert m(2, 128, 64, 128, P, st4, P, P, P, I64x2(64 * 64, 64), None, None) == ERR_UNSUPPORTED   # head_dim
+    assert m(2, 128, 64, 64, None, st4, P, P, P, I64x2(64 * 64, 64), None, None) == ERR_NULL
+    assert m(2, 128, 64, 64, P, (ctypes.c_int64 * 4)(1, 1, 1, 2), P, P, P, I64x2(64 * 64, 64), None, None) == \
+        ERR_UNSUPPORTED
+    assert m(2, 0, 64, 64, P, st4, P, P, P, I64x2(64 * 64, 64), None, None) == OK

@@ -90,7 +90,8 @@ def test_merge_degenerate_forms():
     # a part with no keys changes nothing; with sink -inf one part is returned as is
     a = cp.merge([(o1, l1), empty], sinks)
     b = cp.merge([(o1, l1)], sinks)
-    np.testing.assert_allclose(a[0], b[0], rtol=1e-14) and np.testing.assert_allclose(a[1], b[1], rtol=1e-14)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-14)
     c = cp.merge([(o1, l1)], np.full(4, -np.inf))
     np.testing.assert_allclose(c[0], o1, rtol=1e-14)
     np.testing.assert_allclose(c[1], l1, rtol=1e-14)
