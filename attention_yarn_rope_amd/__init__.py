@@ -19,6 +19,7 @@ from .api import (  # noqa: F401
     attn_decode,
     qkv_proj_rope,
     attn_prefill_shard,
+    prefill_shard_workspace_size,
     attn_merge,
     kv_layout,
     kv_append,

@@ -376,6 +376,13 @@ def qkv_proj_rope(x, wq, bq, wk, bk, wv, bv, table=None, cu_seqlens=None, max_se
     return q, k, v
 
 
+def prefill_shard_workspace_size(q, k):
+    """Workspace bytes of attn_prefill_shard for a query shard q [B, Sq, Hq, D] and key shard k [B, Sk, Hkv, D]."""
+    B, S, Hq, D = q.shape
+    desc = SeqDesc(_lib.BSHD, B, S, S, None, Hq, k.shape[2], D)
+    return _lib.load().gptoss_attn_prefill_shard_workspace_size(ctypes.byref(desc), k.shape[1])
+
+
 def attn_prefill_shard(q, k, v, q_offset, kv_offset, window=0, table=None, softmax_scale=None, out=None, lse=None,
                        workspace=None):
     """One step of a context-parallel prefill: q [B, Sq, Hq, D] at positions q_offset + s against
@@ -391,8 +398,7 @@ def attn_prefill_shard(q, k, v, q_offset, kv_offset, window=0, table=None, softm
         lse = torch.empty((B * S, Hq), dtype=torch.float32, device=q.device)
     lib = _lib.load()
     if workspace is None:
-        need = lib.gptoss_attn_prefill_shard_workspace_size(ctypes.byref(desc), k.shape[1])
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(prefill_shard_workspace_size(q, k), 1), dtype=torch.uint8, device=q.device)
     scale = D ** -0.5 if softmax_scale is None else softmax_scale
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     check("gptoss_attn_prefill_shard", lib.gptoss_attn_prefill_shard(

@@ -423,12 +423,11 @@ gptoss_status gptoss_attn_merge(int32_t num_parts, int32_t tokens, int32_t num_q
   if (tokens == 0) return GPTOSS_OK;
   if (!out || !o_strides || (num_parts > 0 && (!o_parts || !part_strides || !lse_parts)))
     return fail(GPTOSS_ERR_NULL, "out, its strides and (with parts) the parts, their strides and lse are required");
-  if (num_parts > 0 && (part_strides[0] < 0 || part_strides[1] < 0 || part_strides[2] < 0 || part_strides[3] != 1 ||
-                        (reinterpret_cast<uintptr_t>(o_parts) & 1)))
-    return fail(GPTOSS_ERR_UNSUPPORTED, "part strides must be non-negative with the head dim contiguous");
-  if (o_strides[0] < 0 || o_strides[1] < 0 || (o_strides[0] & 1) || (o_strides[1] & 1) ||
-      (reinterpret_cast<uintptr_t>(out) & 3))
-    return fail(GPTOSS_ERR_UNSUPPORTED, "out must be 4-byte aligned with even strides");
+  if (num_parts > 0 && (!strides_ok(part_strides, 3) || part_strides[3] != 1 || !aligned16(o_parts)))
+    return fail(GPTOSS_ERR_UNSUPPORTED,
+                "o_parts must be 16-byte aligned, strides multiples of 8 with the head dim contiguous");
+  if (!strides_ok(o_strides, 2) || !aligned16(out))
+    return fail(GPTOSS_ERR_UNSUPPORTED, "out must be 16-byte aligned with strides multiples of 8");
   MergeParams p;
   memset(&p, 0, sizeof p);
   p.o = static_cast<const uint16_t*>(o_parts);

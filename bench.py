@@ -21,11 +21,14 @@ The backward pass of both layers (dq, dk, dv, dsinks) is timed after the step an
 reported under "backward" (not part of `value`). The q/k/v projections of the
 same tokens (hidden 2880, Linear with bias) with the RoPE in their epilogue are
 timed under "projection", next to torch's linear (hipBLASLt) followed by the
-standalone rotation, as context.
+standalone rotation, as context. One step of a context-parallel prefill (a
+128K-token sequence over 8 ranks: a 16384-token query shard against a
+16384-token key shard) and the merge of 8 partial results are timed under
+"context_parallel" (one GPU's share of the ring; the exchange is not built).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
        python bench.py --profile {prefill-full,prefill-window,decode-full,copy,backward-full,backward-window,
-                                  decode-paged,decode-ring,kv-append,proj-rope,proj} --steps K
+                                  decode-paged,decode-ring,kv-append,proj-rope,proj,cp-step} --steps K
        (the --profile modes run only the named call, for rocprofv3)
 """
 
@@ -227,7 +230,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy",
                                                         "backward-full", "backward-window", "decode-paged",
-                                                        "decode-ring", "kv-append", "proj-rope", "proj"])
+                                                        "decode-ring", "kv-append", "proj-rope", "proj",
+                                                        "cp-step"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -309,6 +313,38 @@ def main():
         log(f"{args.profile}: {args.steps} calls")
         return
 
+    # ---------------- context-parallel prefill: one GPU's ring step and the merge ----------------
+    def cp_calls():
+        n, ranks = 16384, 8
+        sh = wl.prefill_bshd(1, n, seed=61)
+        cq, ck, cv = sh.q.to(dev), sh.k.to(dev), sh.v.to(dev)
+        ctab = gx.rope_table(n * ranks)
+        o = torch.empty_like(cq)
+        lse = torch.empty((n, cq.shape[2]), dtype=torch.float32, device=dev)
+        cws = torch.empty(max(gx.prefill_shard_workspace_size(cq, ck), 1), dtype=torch.uint8, device=dev)
+        parts_o = torch.randn((ranks, n, cq.shape[2], 64), generator=torch.Generator().manual_seed(62)).to(
+            torch.bfloat16).to(dev)
+        parts_l = (torch.randn((ranks, n * cq.shape[2]), generator=torch.Generator().manual_seed(63)) * 2).to(dev)
+        mo = torch.empty((n, cq.shape[2], 64), dtype=torch.bfloat16, device=dev)
+        qo = (ranks - 1) * n
+        return {
+            "offdiag": lambda: gx.attn_prefill_shard(cq, ck, cv, qo, 0, table=ctab, out=o, lse=lse, workspace=cws),
+            "diag": lambda: gx.attn_prefill_shard(cq, ck, cv, qo, qo, table=ctab, out=o, lse=lse, workspace=cws),
+            "merge": lambda: gx.attn_merge(parts_o, parts_l, sinks, out=mo),
+            "flops_offdiag": 4 * 64 * cq.shape[2] * n * n,
+            "flops_diag": wl.prefill_flops([n], 0),
+            "bytes_merge": ranks * n * cq.shape[2] * (64 * 2 + 4) + n * cq.shape[2] * 64 * 2,
+            "n": n, "ranks": ranks,
+        }
+
+    if args.profile == "cp-step":
+        fn = cp_calls()["offdiag"]
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"cp-step: {args.steps} calls")
+        return
+
     # ---------------- backward of both layers (measured beside the step) ----------------
     def backward_calls():
         """One forward with lse per layer, then closures that run each layer's backward."""
@@ -384,6 +420,38 @@ def main():
         log(f"[bench] projection fused {projection_obj['fused']['ms']:.3f} ms "
             f"({projection_obj['fused']['TFLOP/s']:.0f} TFLOP/s)")
         del pc, timer
+
+    cp_obj = None
+    if args.profile is None:
+        cc = cp_calls()
+        timer = Timer(torch)
+        names = ("offdiag", "diag", "merge")
+        for _ in range(args.warmup):
+            for nm in names:
+                cc[nm]()
+        torch.cuda.synchronize()
+        for _ in range(max(args.steps // 4, 3)):
+            for nm in names:
+                timer.run(nm, cc[nm])
+        torch.cuda.synchronize()
+        ms = {nm: timer.mean_ms(nm) for nm in names}
+        cp_obj = {
+            "workload": f"one ring step of a {cc['n'] * cc['ranks']}-token full-causal prefill over {cc['ranks']} "
+                        f"ranks: a {cc['n']}-token query shard (the last rank's) against a {cc['n']}-token key "
+                        "shard, q and k rotated at their global positions, no sink; the merge of "
+                        f"{cc['ranks']} partial results adds it",
+            "offdiag_step": {"ms": round(ms["offdiag"], 4), "flops": cc["flops_offdiag"],
+                             "TFLOP/s": round(cc["flops_offdiag"] / (ms["offdiag"] * 1e-3) / 1e12, 1),
+                             "frac_mfma_peak": round(cc["flops_offdiag"] / (ms["offdiag"] * 1e-3) / 1e12 /
+                                                     PEAK_BF16_TFLOPS, 4)},
+            "diag_step": {"ms": round(ms["diag"], 4), "flops": cc["flops_diag"],
+                          "TFLOP/s": round(cc["flops_diag"] / (ms["diag"] * 1e-3) / 1e12, 1)},
+            "merge": {"ms": round(ms["merge"], 4), "bytes": cc["bytes_merge"],
+                      "GB/s": round(cc["bytes_merge"] / (ms["merge"] * 1e-3) / 1e9, 1)},
+        }
+        log(f"[bench] context-parallel step {ms['offdiag']:.3f} ms (diagonal {ms['diag']:.3f} ms), "
+            f"merge {ms['merge']:.3f} ms")
+        del cc, timer
 
     backward_obj = None
     if args.profile is None and not args.no_backward:
@@ -513,6 +581,7 @@ def main():
         },
         "backward": backward_obj,
         "projection": projection_obj,
+        "context_parallel": cp_obj,
         "decode": decode_obj,
         "cpu_baseline": None,
     }

@@ -344,10 +344,11 @@ gptoss_status gptoss_attn_prefill_shard(const gptoss_seq_desc* desc,
  * gptoss_attn_prefill_shard) and add the per-head sink once:
  *   lse = log(e^sigma_h + sum_p e^{lse_p}),  out = sum_p e^{lse_p - lse} o_p.
  *   o_parts:    bf16 [num_parts, tokens, Hq, 64], element strides part_strides
- *               {part, token, head, 1}.
+ *               {part, token, head, 1} (multiples of 8; 16-byte aligned).
  *   lse_parts:  fp32 [num_parts, tokens * Hq], contiguous (-inf: no keys).
  *   sinks:      fp32 [Hq]; NULL = no sink.
- *   out:        bf16 [tokens, Hq, 64] with o_strides {token, head} (even).
+ *   out:        bf16 [tokens, Hq, 64] with o_strides {token, head} (multiples
+ *               of 8; 16-byte aligned).
  *   lse_out:    optional fp32 [tokens * Hq] (NULL: not written).
  * num_parts = 0 gives out = 0 (lse_out = sigma).
  */
