@@ -37,7 +37,7 @@ namespace {
 
 constexpr int BQ = kPrefillBQ;  // 32 query positions per item
 constexpr int NK = 64;          // keys per KV tile
-constexpr int KS = 72;          // LDS row stride of the K tile (144 B): conflict-free 16 B reads
+constexpr int KS = 80;          // LDS row stride of the K tile (160 B): half the bank conflicts of 144 B (measured)
 constexpr int VS = 80;          // LDS row stride of the V tile (160 B): conflict-free tr16 reads
 constexpr float kSumLimit = 0x1p100f;   // bound of a tile's partial row sum before the reference moves
 constexpr float kRaiseGap = 8.0f;       // the reference moves to a new max more than this far above it

@@ -14,7 +14,9 @@ ring caches for the window layer, and the cache append, under "decode.kv_cache".
 
 Timing uses HIP events recorded on the stream the library launches on, around
 every call inside the timed region; the whole region is bracketed by device
-synchronisation. The CPU baseline is the fp64 oracle on a time-bounded sample
+synchronisation. Every section runs W untimed warm-up iterations first (default
+100): from idle, this GPU needs a few tens of milliseconds of sustained load
+before its clock settles, and calls timed earlier run up to 20 % slower. The CPU baseline is the fp64 oracle on a time-bounded sample
 of query rows of the same workload, on this host's cores.
 
 The backward pass of both layers (dq, dk, dv, dsinks) is timed after the step and
@@ -26,7 +28,7 @@ standalone rotation, as context. One step of a context-parallel prefill (a
 16384-token key shard) and the merge of 8 partial results are timed under
 "context_parallel" (one GPU's share of the ring; the exchange is not built).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward] [--settle SECONDS]
        python bench.py --profile {prefill-full,prefill-window,decode-full,copy,backward-full,backward-window,
                                   decode-paged,decode-ring,kv-append,proj-rope,proj,cp-step} --steps K
        (the --profile modes run only the named call, for rocprofv3)
@@ -109,6 +111,21 @@ class Timer:
     def mean_ms(self, name):
         v = [s.elapsed_time(e) for s, e in self.pairs.get(name, [])]
         return sum(v) / len(v) if v else float("nan")
+
+
+def settle_clock(torch, dev, seconds):
+    """Sustained bf16 matrix-core load for `seconds`, so that a profiled kernel's launches all run at
+    the settled clock (from idle this GPU needs tens of milliseconds of load to reach it)."""
+    if seconds <= 0:
+        return
+    a = torch.randn((4096, 4096), device=dev).to(torch.bfloat16)
+    torch.mm(a, a)   # library set-up happens here, outside the timed load
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            torch.mm(a, a)
+        torch.cuda.synchronize()
 
 
 def cpu_baseline(inp, budget_s):
@@ -222,7 +239,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle", type=float, default=0.2,
+                    help="--profile modes: seconds of matrix-core load before the profiled calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-decode", action="store_true")
@@ -280,6 +299,7 @@ def main():
 
     if args.profile in ("prefill-full", "prefill-window"):
         fn = call_full if args.profile == "prefill-full" else call_win
+        settle_clock(torch, dev, args.settle)
         for _ in range(args.steps):
             fn()
         torch.cuda.synchronize()
@@ -307,6 +327,7 @@ def main():
 
     if args.profile in ("proj-rope", "proj"):
         fn = projection_calls()["fused" if args.profile == "proj-rope" else "unrotated"]
+        settle_clock(torch, dev, args.settle)
         for _ in range(args.steps):
             fn()
         torch.cuda.synchronize()
@@ -339,6 +360,7 @@ def main():
 
     if args.profile == "cp-step":
         fn = cp_calls()["offdiag"]
+        settle_clock(torch, dev, args.settle)
         for _ in range(args.steps):
             fn()
         torch.cuda.synchronize()
@@ -361,6 +383,7 @@ def main():
 
     if args.profile in ("backward-full", "backward-window"):
         fn = backward_calls()["full" if args.profile == "backward-full" else "window128"]
+        settle_clock(torch, dev, args.settle)
         for _ in range(args.steps):
             fn()
         torch.cuda.synchronize()
@@ -397,14 +420,15 @@ def main():
         pc = projection_calls()
         timer = Timer(torch)
         names = ("fused", "unrotated", "torch_linear_rope_qk")
-        for _ in range(args.warmup):
-            for n in names:
+        # each call type in its own block of K calls after its warm-up (interleaving the three
+        # measured the first one up to 20 % slower than the same kernel run back to back)
+        for n in names:
+            for _ in range(args.warmup):
                 pc[n]()
-        torch.cuda.synchronize()
-        for _ in range(args.steps):
-            for n in names:
+            torch.cuda.synchronize()
+            for _ in range(args.steps):
                 timer.run(n, pc[n])
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         pfl = pc["flops"]
         projection_obj = {
             "workload": f"q/k/v projections of the dense prefill's {q.shape[0] * S} tokens: hidden 2880 -> "
@@ -500,6 +524,7 @@ def main():
                                           workspace=dws)
 
         if args.profile == "decode-full":
+            settle_clock(torch, dev, args.settle)
             for _ in range(args.steps):
                 dec(0)()
             torch.cuda.synchronize()
@@ -508,6 +533,7 @@ def main():
         kvc = kv_cache_calls(torch, gx, wl, dev, dq, kc, vc, lens, dsinks, dtable, dinp.lengths, d_out, k, v)
         if args.profile in ("decode-paged", "decode-ring", "kv-append"):
             fn = kvc[{"decode-paged": "paged_full", "decode-ring": "ring_window", "kv-append": "append_1"}[args.profile]]
+            settle_clock(torch, dev, args.settle)
             for _ in range(args.steps):
                 fn()
             torch.cuda.synchronize()
