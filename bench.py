@@ -19,6 +19,9 @@ synchronisation. Every section runs W untimed warm-up iterations first (default
 before its clock settles, and calls timed earlier run up to 20 % slower. The CPU baseline is the fp64 oracle on a time-bounded sample
 of query rows of the same workload, on this host's cores.
 
+The same two layers over 16 packed THD sequences (lengths uniform in [128, 8192])
+and over one 131072-token sequence are timed under "prefill_thd_and_long".
+
 The backward pass of both layers (dq, dk, dv, dsinks) is timed after the step and
 reported under "backward" (not part of `value`). The q/k/v projections of the
 same tokens (hidden 2880, Linear with bias) with the RoPE in their epilogue are
@@ -247,6 +250,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--k-rotation", default="auto", choices=["auto", "fused", "separate"])
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip the THD and 128K-token prefill timings")
     ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy",
                                                         "backward-full", "backward-window", "decode-paged",
                                                         "decode-ring", "kv-append", "proj-rope", "proj",
@@ -414,6 +419,62 @@ def main():
         log(f"[bench] prefill step {ms_step:.3f} ms (full {ms_full:.3f} ms, window {ms_win:.3f} ms, "
             f"table {ms_table:.4f} ms)")
         del timer
+
+    other_obj = None
+    if args.profile is None and not args.no_other_prefill:
+        # the same two layers over packed THD sequences (the varlen scheduler) and over one
+        # 131072-token sequence (the 128K context); parity cases in the tests, timed here
+        other_obj = {}
+        ti = wl.thd()
+        tq, tk, tv, ts = (t.to(dev) for t in (ti.q, ti.k, ti.v, ti.sinks))
+        tcu = ti.cu_seqlens.to(dev)
+        ttab = gx.rope_table(ti.max_seqlen)
+        tout = torch.empty_like(tq)
+        tws = torch.empty(max(gx.prefill_workspace_size(tq, tk, cu_seqlens=tcu, max_seqlen=ti.max_seqlen), 1),
+                          dtype=torch.uint8, device=dev)
+        thd_calls = {w: (lambda w=w: gx.attn_prefill(tq, tk, tv, ts, window=w, table=ttab, cu_seqlens=tcu,
+                                                     max_seqlen=ti.max_seqlen, out=tout, workspace=tws))
+                     for w in (0, WINDOW)}
+        timer = Timer(torch)
+        for w, fn in thd_calls.items():
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            for _ in range(args.steps):
+                timer.run(w, fn)
+            torch.cuda.synchronize()
+        other_obj["thd"] = {"workload": f"THD: {len(ti.lengths)} packed sequences, lengths uniform in [128, 8192] "
+                                        f"(T = {sum(ti.lengths)}), Hq=64 Hkv=8 D=64, bf16"}
+        for w, nm in ((0, "full"), (WINDOW, "window128")):
+            ms = timer.mean_ms(w)
+            fl = wl.prefill_flops(ti.lengths, w)
+            other_obj["thd"][nm] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1), "flops": fl}
+        del tq, tk, tv, tout, tws, thd_calls, timer
+        li = wl.long_context()
+        lq, lk, lv, lsk = (t.to(dev) for t in (li.q, li.k, li.v, li.sinks))
+        del li
+        ltab = gx.rope_table(lq.shape[1])
+        lout = torch.empty_like(lq)
+        lws = torch.empty(max(gx.prefill_workspace_size(lq, lk), 1), dtype=torch.uint8, device=dev)
+        timer = Timer(torch)
+        n_long = max(min(args.steps, 3), 1)
+        for w in (0, WINDOW):
+            fn = (lambda w=w: gx.attn_prefill(lq, lk, lv, lsk, window=w, table=ltab, out=lout, workspace=lws))
+            for _ in range(2 if w == 0 else args.warmup):   # a full-layer call is ~0.15 s of load by itself
+                fn()
+            torch.cuda.synchronize()
+            for _ in range(n_long):
+                timer.run(w, fn)
+            torch.cuda.synchronize()
+        other_obj["long"] = {"workload": f"one sequence of {lq.shape[1]} tokens (B=1), Hq=64 Hkv=8 D=64, bf16",
+                             "timed_calls": n_long}
+        for w, nm in ((0, "full"), (WINDOW, "window128")):
+            ms = timer.mean_ms(w)
+            fl = wl.prefill_flops([lq.shape[1]], w)
+            other_obj["long"][nm] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1), "flops": fl}
+        log(f"[bench] THD full {other_obj['thd']['full']['ms']:.3f} ms, window {other_obj['thd']['window128']['ms']:.3f}"
+            f" ms; 128K full {other_obj['long']['full']['ms']:.1f} ms, window {other_obj['long']['window128']['ms']:.3f} ms")
+        del lq, lk, lv, lout, lws, timer
 
     projection_obj = None
     if args.profile is None:
@@ -605,6 +666,7 @@ def main():
                           "flops": flops_win, "bytes": bytes_prefill},
             "table_ms": round(ms_table, 5),
         },
+        "prefill_thd_and_long": other_obj,
         "backward": backward_obj,
         "projection": projection_obj,
         "context_parallel": cp_obj,

@@ -118,6 +118,30 @@ def test_merge_against_oracle():
     assert not none.any()
 
 
+@pytest.mark.parametrize("P", [1, 8, 9, 17])
+def test_merge_part_batches_and_strides(P):
+    """Part counts around the kernel's batch of 8 loads (one part, one full batch, a batch and
+    one more, three batches), with the parts a view into a larger buffer and a strided output."""
+    g = torch.Generator().manual_seed(80 + P)
+    T, H = 77, 16
+    buf = torch.randn((P, T + 3, H, 64), generator=g).to(torch.bfloat16)
+    lse = torch.randn((P, T * H), generator=g) * 4
+    lse[P // 2, ::5] = -float("inf")
+    sinks = torch.randn(H, generator=g)
+    sinks[3] = -float("inf")
+    o = buf.cuda()[:, :T]                               # part stride (T + 3) * H * 64
+    big = torch.zeros((T, H, 72), dtype=torch.bfloat16, device="cuda")
+    out = big[..., :64]                                 # token stride H * 72, head stride 72
+    lo = torch.empty(T * H, dtype=torch.float32, device="cuda")
+    say(f"[gpu] merge P={P} strided parts and output")
+    gx.attn_merge(o, lse.cuda(), sinks.cuda(), out=out, lse_out=lo)
+    parts = [(np64(buf[p, :T]), np64(lse[p]).reshape(T, H)) for p in range(P)]
+    ro, rl = cp.merge(parts, np64(sinks))
+    assert_close(out, ro, f"merge P={P}")
+    assert not big[..., 64:].any(), "the merge wrote past the rows' 64 dims"
+    np.testing.assert_allclose(np64(lo).reshape(T, H), rl, rtol=1e-5, atol=1e-5)
+
+
 def test_ring_step_at_128k(table):
     """One ring step of the 128K-token prefill split over 8 ranks (16384 tokens each): the last
     rank's queries against the first rank's keys (all visible) and against its own keys (the
