@@ -221,6 +221,33 @@ def kv_cache_bench(torch, wl, kvc, args, lengths, b_full, b_win):
             timer.run(n, kvc[n])
     torch.cuda.synchronize()
     ms = {n: timer.mean_ms(n) for n in names}
+
+    # one decode step of a full + window layer pair as a serving loop runs it (append the new
+    # tokens to the paged pool and the rings, then both decodes), eager and as a HIP graph
+    # replay; K steps back to back between two events
+    def step():
+        kvc["append_1"]()
+        kvc["paged_full"]()
+        kvc["ring_window"]()
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    step_ms = {}
+    for nm, fn in (("eager", step), ("graph", graph.replay)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            fn()
+        e.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        step_ms[nm] = s.elapsed_time(e) / args.steps
+    del graph
     T = kvc["prompt_tokens"]
     b_prompt = T * 8 * 64 * 2 * 4 + 4096 * 64 * 2   # read k, v; write k, v; table rows
     return {
@@ -233,6 +260,9 @@ def kv_cache_bench(torch, wl, kvc, args, lengths, b_full, b_win):
         "ring_window_layer": {"ms": round(ms["ring_window"], 4),
                               "GB/s": round(b_win / (ms["ring_window"] * 1e-3) / 1e9, 1)},
         "append_1_token_ms": round(ms["append_1"], 4),
+        "decode_step": {"what": "append 1 token x 64 sequences (pool and rings) + paged full-layer decode + ring "
+                                "window-layer decode, K steps back to back",
+                        "eager_ms": round(step_ms["eager"], 4), "hip_graph_ms": round(step_ms["graph"], 4)},
         "append_prompt": {"ms": round(ms["append_prompt"], 4), "bytes": b_prompt,
                           "GB/s": round(b_prompt / (ms["append_prompt"] * 1e-3) / 1e9, 1)},
     }
