@@ -243,9 +243,24 @@ void prefill_kernel(PrefillParams p) {
   }
   __syncthreads();
 
+  // Window items whose keys start W - 1 before their first query (a multiple-of-32
+  // window, not a shard): the first 32-key step holds key j visible to query row i
+  // iff j >= i, and the step W / 32 later iff j < i; every step between is fully
+  // visible. ge[kb][r][c] is that test for this lane's scores (key kb*16 + 4*grp + r,
+  // row col + 16c), computed once instead of comparing positions in those steps.
+  bool ge[2][4][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ge[kb][r][c] = kb * 16 + 4 * grp + r >= col + 16 * c;
+
   // ---- one compute step over NKT keys (64: a whole tile, 32: half of one) whose
-  // K and V rows start at kt and vt in LDS; tile0 = position of the first key ----
-  auto compute = [&](auto nkt_tag, const bf16_t* kt, const bf16_t* vt, int tile0) __attribute__((always_inline)) {
+  // K and V rows start at kt and vt in LDS; tile0 = position of the first key;
+  // pat: 0 = general mask, 1 / 2 = the window's first / last step (see ge) ----
+  auto compute = [&](auto nkt_tag, const bf16_t* kt, const bf16_t* vt, int tile0, int pat)
+      __attribute__((always_inline)) {
     constexpr int NKT = decltype(nkt_tag)::value;
     constexpr int KBN = NKT / 16;   // 16-key blocks of S^T
     constexpr int KSN = NKT / 32;   // 32-key slices of P^T (one PV MFMA each)
@@ -272,7 +287,19 @@ void prefill_kernel(PrefillParams p) {
     // before its queries, and then lo = qpos - kv_hi + 1 hides the rows past the
     // keys (they read as zeros) ----
     const bool full = (tile0 + NKT - 1 <= qk0) && (W == 0 || qklast - tile0 < W) && (tile0 + NKT <= kv_hi);
-    if (!full) {
+    if constexpr (NKT == 32) {
+      if (!full && pat != 0) {
+        const bool first = pat == 1;
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+              sacc[kb][cb][r] = (ge[kb][r][cb & 1] == first) ? sacc[kb][cb][r] : -INFINITY;
+      }
+    }
+    if (!full && pat == 0) {
 #pragma unroll
       for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
@@ -364,13 +391,16 @@ void prefill_kernel(PrefillParams p) {
     // every tile is in LDS, rows in key order: 32-key steps, and only the steps
     // holding keys of the item (a 159-key window span takes 5 steps, not 6)
     const int nsteps = (kv_hi - kv_lo + 31) / 32;
-    for (int u = 0; u < nsteps; ++u)
-      compute(KeyCount<32>(), lds_k + u * 32 * KS, lds_v + u * 32 * VS, kv_lo + 32 * u);
+    const bool fixed = W > 0 && (W & 31) == 0 && p.q_shift == 0 && qk0 >= W - 1;   // kv_lo = qk0 - W + 1
+    for (int u = 0; u < nsteps; ++u) {
+      const int pat = fixed ? (u == 0 ? 1 : (u == W / 32 ? 2 : 0)) : 0;
+      compute(KeyCount<32>(), lds_k + u * 32 * KS, lds_v + u * 32 * VS, kv_lo + 32 * u, pat);
+    }
   } else {
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
       if (t + 1 < ntiles) load_tile(t + 1, st[0]);
-      compute(KeyCount<NK>(), lds_k + buf * NK * KS, lds_v + buf * NK * VS, kv_lo + t * NK);
+      compute(KeyCount<NK>(), lds_k + buf * NK * KS, lds_v + buf * NK * VS, kv_lo + t * NK, 0);
       if (t + 1 < ntiles) store_tile(buf ^ 1, st[0]);
       __syncthreads();
     }

@@ -63,6 +63,24 @@ def test_window_staging_boundary(table, window):
     assert_close(out, _ref_bshd(inp, window), f"bshd B=2 S=700 W={window}")
 
 
+@pytest.mark.parametrize("window", [32, 64, 96, 160])
+def test_window_fixed_step_masks(table, window):
+    """Windows that are multiples of 32 use fixed masks for the first and last key step of
+    every 32-query item whose keys start W - 1 before it (not the first items of a sequence):
+    BSHD with a ragged tail, and THD sequences that start at and after such offsets."""
+    inp = wl.prefill_bshd(2, 517, seed=500 + window)
+    say(f"[gpu] prefill fixed window masks W={window}")
+    out = _run_bshd(inp, window, table)
+    assert_close(out, _ref_bshd(inp, window), f"bshd B=2 S=517 W={window}")
+    t = wl.prefill_thd(0, 0, 0, seed=510 + window, lengths=[window + 1, 300, 0, 31, 400])
+    cu = t.cu_seqlens.cuda()
+    out = gx.attn_prefill(t.q.cuda(), t.k.cuda(), t.v.cuda(), t.sinks.cuda(), window=window, table=table,
+                          cu_seqlens=cu, max_seqlen=t.max_seqlen)
+    ref = oracle.prefill_thd(np64(t.q), np64(t.k), np64(t.v), t.cu_seqlens.numpy(), np64(t.sinks), TAU, window,
+                             CFG)
+    assert_close(out, ref, f"thd W={window}")
+
+
 @pytest.mark.parametrize("hkv", [1, 2])
 def test_other_group_counts(table, hkv):
     inp = wl.prefill_bshd(1, 300, seed=300 + hkv, hq=8 * hkv, hkv=hkv)
