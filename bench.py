@@ -32,7 +32,7 @@ standalone rotation, as context. One step of a context-parallel prefill (a
 "context_parallel" (one GPU's share of the ring; the exchange is not built).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward] [--settle SECONDS]
-       python bench.py --profile {prefill-full,prefill-window,decode-full,copy,backward-full,backward-window,
+       python bench.py --profile {step,prefill-full,prefill-window,decode-full,copy,backward-full,backward-window,
                                   decode-paged,decode-ring,kv-append,proj-rope,proj,cp-step} --steps K
        (the --profile modes run only the named call, for rocprofv3)
 """
@@ -282,7 +282,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip the THD and 128K-token prefill timings")
-    ap.add_argument("--profile", default=None, choices=["prefill-full", "prefill-window", "decode-full", "copy",
+    ap.add_argument("--profile", default=None, choices=["step", "prefill-full", "prefill-window", "decode-full", "copy",
                                                         "backward-full", "backward-window", "decode-paged",
                                                         "decode-ring", "kv-append", "proj-rope", "proj",
                                                         "cp-step"])
@@ -331,6 +331,17 @@ def main():
     def call_win():
         gx.attn_prefill(q, k, v, sinks, window=WINDOW, table=table, out=o_win, workspace=ws,
                         k_rotation=args.k_rotation)
+
+    if args.profile == "step":
+        # the timed step's exact call sequence (table, full layer, window layer), for rocprofv3
+        settle_clock(torch, dev, args.settle)
+        for _ in range(args.steps):
+            gx.rope_table(S, out=table)
+            call_full()
+            call_win()
+        torch.cuda.synchronize()
+        log(f"step: {args.steps} steps")
+        return
 
     if args.profile in ("prefill-full", "prefill-window"):
         fn = call_full if args.profile == "prefill-full" else call_win
