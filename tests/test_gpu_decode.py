@@ -80,3 +80,32 @@ def test_decode_deterministic(table):
     inp = wl.decode(0, 0, 0, seed=25, max_len=5000, lengths=[5000, 4000])
     a, b = _run(inp, 0, table), _run(inp, 0, table)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_decode_128k_context(window):
+    """The longest context (131072 positions): a full cache, a ragged one and a one-token one,
+    from a contiguous cache and from a shuffled pool of 64-row pages holding the same rows
+    (bit-identical to the contiguous decode for the full layer)."""
+    lengths = [131072, 77777, 1]
+    inp = wl.decode(0, 0, 0, seed=26, max_len=131072, lengths=lengths)
+    table = gx.rope_table(131072)
+    say(f"[gpu] decode 128K context window={window}")
+    out = _run(inp, window, table)
+    assert_close(out, _ref(inp, window), f"decode 128K W={window}")
+    N, Lmax, ps = len(lengths), 131072, 64
+    npages = N * Lmax // ps
+    perm = torch.randperm(npages, generator=torch.Generator().manual_seed(27))
+    kc, vc = inp.k_cache.cuda(), inp.v_cache.cuda()
+    k_pool = torch.empty((npages, ps, 8, 64), dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.empty_like(k_pool)
+    k_pool[perm.cuda()] = kc.reshape(npages, ps, 8, 64)
+    v_pool[perm.cuda()] = vc.reshape(npages, ps, 8, 64)
+    del kc, vc
+    bt = perm.to(torch.int32).reshape(N, Lmax // ps).contiguous().cuda()
+    paged = gx.attn_decode_kv(inp.q.cuda(), k_pool, v_pool, inp.cache_seqlens.cuda(), inp.sinks.cuda(), kind="paged",
+                              block_table=bt, window=window, table=table)
+    if window == 0:
+        assert torch.equal(paged, out), "paged decode differs from the contiguous decode of the same rows"
+    else:
+        assert_close(paged, _ref(inp, window), f"paged decode 128K W={window}")
