@@ -11,7 +11,11 @@
  *     synchronises: the caller owns every buffer (inputs, outputs, table,
  *     workspace) and keeps it alive until the work on `stream` has finished.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *     Every call only enqueues kernels on it and returns.
+ *     Every call only enqueues kernels on it and returns. No call clears
+ *     memory with a memset, and every length and work list is read or built
+ *     on the device, so the calls may be captured in a HIP graph and
+ *     replayed with new buffer contents (new lengths included) as long as the
+ *     host-side arguments stay the same.
  *   - bf16 means IEEE bfloat16 stored as uint16; fp32 sinks.
  *   - Strides are in ELEMENTS, not bytes; the last (head_dim) dimension must
  *     be contiguous. Outputs of gptoss_rope_qk are contiguous; the attention
