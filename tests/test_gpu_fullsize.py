@@ -106,6 +106,36 @@ def test_long_context():
     del out
 
 
+def test_over_2g_elements():
+    """B=4, S=131072: q and the output hold 2^31 elements each (4 GiB), past any 32-bit element
+    offset. The inputs are drawn on the GPU from a seeded generator; sampled rows of the last
+    sequence (the largest offsets) are checked against the oracle for the window layer (64 rows)
+    and the full-causal layer (8 rows)."""
+    B, S = 4, 131072
+    g = torch.Generator(device="cuda").manual_seed(77)
+
+    def draw(shape):
+        t = torch.empty((B,) + shape, dtype=torch.bfloat16, device="cuda")
+        for b in range(B):
+            t[b] = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        return t
+
+    q, k, v = draw((S, 64, 64)), draw((S, 8, 64)), draw((S, 8, 64))
+    s = torch.randn(64, generator=g, device="cuda", dtype=torch.float32)
+    assert q.numel() == 2 ** 31
+    table = gx.rope_table(S)
+    rows = [0, 1, 127, 128, 65536, S - 1] + torch.randperm(S, generator=torch.Generator().manual_seed(78))[:58].tolist()
+    rows = np.array(sorted(set(rows)))
+    q3, k3, v3, s3 = q[3].cpu(), k[3].cpu(), v[3].cpu(), s.cpu()
+    say("[gpu] B=4 S=131072 (2^31-element q) window=128")
+    out = gx.attn_prefill(q, k, v, s, window=128, table=table)
+    _check_rows(out[3].cpu(), q3, k3, v3, s3, 128, rows, "B=4 S=131072 W=128, last sequence")
+    del out
+    say("[gpu] B=4 S=131072 (2^31-element q) window=0")
+    out = gx.attn_prefill(q, k, v, s, window=0, table=table)
+    _check_rows(out[3].cpu(), q3, k3, v3, s3, 0, rows[[0, 1, 2, 3, 4, -3, -2, -1]], "B=4 S=131072 W=0, last sequence")
+
+
 @pytest.mark.parametrize("window", [0, 128])
 def test_decode_64_sequences(window):
     say(f"[gpu] decode 64 sequences window={window}")
