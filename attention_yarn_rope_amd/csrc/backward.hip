@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   const uint32_t voff = (uint32_t)(srow * vrow_b + 16 * scc);
   uint4 sk, sv;
   auto load_tile = [&](int t) __attribute__((always_inline)) {
-    const int rows = kv_hi - (kv_lo + t * NK);
+    const int rows = min(kv_hi - (kv_lo + t * NK), NK);   // the tile's own rows: the range stays < 2^31 bytes
     sk = ldb16(make_rsrc(k_tile0 + (int64_t)t * NK * krow_b, (rows - 1) * krow_b + 2 * kHeadDim), koff);
     sv = ldb16(make_rsrc(v_tile0 + (int64_t)t * NK * vrow_b, (rows - 1) * vrow_b + 2 * kHeadDim), voff);
   };

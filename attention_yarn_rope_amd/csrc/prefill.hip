@@ -22,11 +22,12 @@
 // from the row-major V tile in LDS through ds_read_b64_tr_b16.
 //
 // Softmax in log2 units against a per-row reference seeded with the sink
-// logit (the sink term exp(sigma - ref) = 1 starts the row sum); the reference
-// only moves in a rare fallback (a tile's partial row sum beyond 2^100), so
-// the hot loop has no running max and no accumulator rescale. Tiles fully
-// visible to every query of the item skip the mask; tiles fully hidden are
-// never visited.
+// logit (the sink term exp(sigma - ref) = 1 starts the row sum); a row with no
+// sink term (sigma = -inf, or a shard of the keys) takes the largest score of
+// the first step in which it sees a key. The reference then only moves in a
+// rare fallback (a tile's partial row sum beyond 2^100), so the hot loop has
+// no running max and no accumulator rescale. Tiles fully visible to every
+// query of the item skip the mask; tiles fully hidden are never visited.
 #include <type_traits>
 
 #include "common.h"
@@ -145,10 +146,11 @@ void prefill_kernel(PrefillParams p) {
   const uint32_t koff = (uint32_t)(srow * krow_b + 16 * scc);
   const uint32_t voff = (uint32_t)(srow * vrow_b + 16 * scc);
   // A tile past the item's last one gets an empty range: its loads return
-  // zeros without touching memory.
+  // zeros without touching memory. The range covers at most the tile's own NK
+  // rows, so it stays below 2^31 bytes for any sequence length.
   struct Stage { uint4 k1, k2, v1, v2, c, s; };
   auto load_tile = [&](int t, Stage& st) {
-    const int rows = kv_hi - (kv_lo + t * NK);   // keys of the item from this tile on
+    const int rows = min(kv_hi - (kv_lo + t * NK), NK);   // keys of the item in this tile
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_tile0 + (int64_t)t * NK * krow_b, (rows - 1) * krow_b + 2 * kHeadDim);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_tile0 + (int64_t)t * NK * vrow_b, (rows - 1) * vrow_b + 2 * kHeadDim);
     st.k1 = ldb16(rk, koff); st.v1 = ldb16(rv, voff);
@@ -215,6 +217,8 @@ void prefill_kernel(PrefillParams p) {
     sink_raw[cb] = __ldg(p.sinks + head);
   }
   float ref[CB], lsum[CB];
+  bool unset[CB];        // column without a sink term whose reference is not set yet
+  bool seeding = false;  // wave-uniform: some column of the wave is unset
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     uint4 y1 = qx[cb][0], y2 = qx[cb][1];
@@ -222,12 +226,17 @@ void prefill_kernel(PrefillParams p) {
     qf[cb][0] = as_bf16x8(y1);
     qf[cb][1] = as_bf16x8(y2);
     // reference = the sink logit (log2 units); the sink term exp2(sigma - ref) = 1
-    // is counted once, in lane group 0. A sink of -inf contributes 0 (reference 0).
-    const float sink = p.no_sink ? -INFINITY : sink_raw[cb] * kLog2e;   // no sink: a shard of the keys
+    // is counted once, in lane group 0. Without a sink term (sigma = -inf, or a
+    // shard of the keys) the reference is taken from the first step holding a
+    // visible key of the column: its largest score (see compute).
+    const float sink = p.no_sink ? -INFINITY : sink_raw[cb] * kLog2e;
     const bool has_sink = sink > -INFINITY;
     ref[cb] = has_sink ? sink : 0.0f;
     lsum[cb] = (grp == 0 && has_sink) ? 1.0f : 0.0f;
+    unset[cb] = !has_sink;
+    seeding |= !has_sink;
   }
+  seeding = __any(seeding);
 
   f32x4_t oacc[4][CB];  // [d block][column block]
 #pragma unroll
@@ -313,6 +322,29 @@ void prefill_kernel(PrefillParams p) {
             sacc[kb][cb][r] = vis ? sacc[kb][cb][r] : -INFINITY;
           }
         }
+    }
+
+    // ---- a column without a sink term takes its reference from the first step in
+    // which it sees a key: the largest score of that step, so the step's sum is at
+    // least 1 and no later exponent can underflow the whole row. Rows whose logits
+    // all lie far below 0 would otherwise sum to 0 against a fixed reference. ----
+    if (seeding) {   // wave-uniform; only while some column of the wave is unset
+      bool left = false;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v = __builtin_fmaxf(v, sacc[kb][cb][r] * sl);
+        const float mt = wave_xor_max(v);          // the column's max (log2 units), -inf if no key
+        if (unset[cb] && mt > -INFINITY) {         // uniform across the 4 lanes of the column
+          ref[cb] = mt;
+          unset[cb] = false;
+        }
+        left |= unset[cb];
+      }
+      seeding = __any(left);
     }
 
     // ---- online softmax against a fixed reference (log2 units) ----

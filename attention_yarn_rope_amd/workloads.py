@@ -161,6 +161,20 @@ def ring_decode(lengths, slots, seed, hq=HQ, hkv=HKV, d=HEAD_DIM, name=None):
                   lengths=lengths)
 
 
+def far_below(lead_q, lead_k, spread, seed, hq=HQ, hkv=HKV, d=HEAD_DIM):
+    """Already-rotated q, k whose scaled dot products all lie near -512, and v.
+
+    q = -8 + spread * N(0, 1) and k = +8 + spread * N(0, 1) in every dimension,
+    v ~ N(0, 1), all rounded to bf16: with scale 1/8 and width 64 every logit is
+    -512 plus a spread of a few units (exactly -512 for spread 0). Draw order:
+    q, k, v. Returns (q [lead_q, Hq, D], k [lead_k, Hkv, D], v [lead_k, Hkv, D])."""
+    g = torch.Generator().manual_seed(seed)
+    q = (-8.0 + spread * torch.randn(tuple(lead_q) + (hq, d), generator=g)).to(torch.bfloat16)
+    k = (8.0 + spread * torch.randn(tuple(lead_k) + (hkv, d), generator=g)).to(torch.bfloat16)
+    v = _randn_bf16(tuple(lead_k) + (hkv, d), g)
+    return q, k, v
+
+
 def new_tokens(num_seqs, num_new, seed, hkv=HKV, d=HEAD_DIM):
     """k and v of the newest tokens [N, num_new, Hkv, D] (un-rotated k), bf16."""
     g = torch.Generator().manual_seed(seed)

@@ -194,3 +194,20 @@ def test_backward_full_size_sampled(table, window):
                      grad_close(dk[b, lo:hi], ref["dk"], n["dk"], f"W={window} dk keys {lo}..{hi - 1}"),
                      grad_close(dv[b, lo:hi], ref["dv"], n["dv"], f"W={window} dv keys {lo}..{hi - 1}")],
                     f"full size W={window}")
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_backward_no_sink_far_below_zero(window):
+    """sigma = -inf with every logit near -512 (already-rotated q = -8 + a, k = 8 + b): the
+    forward's lse must be each row's own log-sum-exp, not -inf, for the gradients to be right."""
+    q, k, v = wl.far_below((1, 300), (1, 300), 0.5, seed=850 + window)
+    sinks = torch.full((64,), -float("inf"))
+    dout = wl.grad_out((1, 300, 64, 64), 1850 + window)
+    say(f"[gpu] backward, no sink, logits near -512, W={window}")
+    qc, kc, vc, sc = q.cuda(), k.cuda(), v.cuda(), sinks.cuda()
+    o, lse = gx.attn_prefill_lse(qc, kc, vc, sc, window=window)
+    grads = gx.attn_prefill_backward(qc, kc, vc, sc, o, dout.cuda(), lse, window=window)
+    ref = oracle.prefill_bshd_backward(np64(q), np64(k), np64(v), np64(sinks), TAU, window, np64(dout),
+                                       rotate_qk=False, with_noise=True)
+    _check((o, lse) + tuple(grads), ref, f"no sink far below W={window}")
+    assert torch.all(grads[3] == 0)
