@@ -24,6 +24,7 @@ from .api import (  # noqa: F401
     kv_layout,
     kv_append,
     attn_decode_kv,
+    attn_decode_kv_noalloc,
     decode_kv_workspace_size,
     prefill_workspace_size,
     prefill_backward_workspace_size,

@@ -77,6 +77,9 @@ SIGNATURES = {
     "gptoss_attn_decode_kv": (ctypes.c_int, [ctypes.POINTER(KVLayout), c_i32, c_i32, c_i32, c_i32, c_vp, I64x2,
                                              c_vp, c_vp, c_vp, c_i32, c_vp, c_f32, c_i32, c_vp, c_i32, c_i32,
                                              c_vp, I64x2, c_vp, c_size, c_i32, c_vp]),
+    "gptoss_attn_decode_kv_noalloc": (ctypes.c_int, [ctypes.POINTER(KVLayout), c_i32, c_i32, c_i32, c_i32, c_vp,
+                                                     I64x2, c_vp, c_vp, c_vp, c_i32, c_vp, c_f32, c_i32, c_vp,
+                                                     c_i32, c_i32, c_vp, I64x2, c_i32, c_vp]),
     "gptoss_attn_decode": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, I64x2, c_vp, c_vp, I64x3,
                                           c_vp, c_i32, c_vp, c_f32, c_i32, c_vp, c_i32, c_i32, c_vp, I64x2,
                                           c_vp, c_size, c_i32, c_vp]),

@@ -330,6 +330,32 @@ def attn_decode_kv(q, k_cache, v_cache, cache_seqlens, sinks, kind="contiguous",
     return out
 
 
+def attn_decode_kv_noalloc(q, k_cache, v_cache, cache_seqlens, sinks, kind="contiguous", block_table=None,
+                           window=0, table=None, max_seqlen=None, softmax_scale=None, num_splits=0, out=None):
+    """attn_decode_kv with no workspace: the library keeps the split partials in its own fixed
+    per-GPU scratch (gptoss_attn_decode_kv_noalloc). Allocates only ``out`` when it is not given."""
+    _bf16(q, "q"), _bf16(k_cache, "k_cache"), _bf16(v_cache, "v_cache")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda:
+        raise TypeError("cache_seqlens must be a CUDA int32 tensor")
+    _sinks(sinks)
+    N, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    lay = kv_layout(k_cache, kind, block_table)
+    if max_seqlen is None:
+        max_seqlen = _cache_max_seqlen(kind, k_cache, block_table, table)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
+    check("gptoss_attn_decode_kv_noalloc", _lib.load().gptoss_attn_decode_kv_noalloc(
+        ctypes.byref(lay), N, Hq, Hkv, D, _ptr(q), I64x2(q.stride(0), q.stride(1)), _ptr(k_cache), _ptr(v_cache),
+        _ptr(cache_seqlens), int(max_seqlen), _ptr(sinks), float(scale), int(window), tptr, trows, tdim,
+        _ptr(out), I64x2(out.stride(0), out.stride(1)), int(num_splits), _stream()))
+    return out
+
+
 def qkv_proj_rope(x, wq, bq, wk, bk, wv, bv, table=None, cu_seqlens=None, max_seqlen=None, out=None):
     """q, k, v = x W^T + b (rounded to bf16), q and k then rotated with the table (None: not rotated).
 

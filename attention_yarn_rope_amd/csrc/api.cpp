@@ -579,9 +579,9 @@ static int32_t decode_fixed_chunk(int32_t eff_len, int32_t num_splits) {
 }
 
 // Upper bound of the splits any call with these sizes uses: the planned split
-// length is at least kDecodeMinChunk keys.
-static int64_t decode_split_cap(int32_t max_cache_len, int32_t num_splits) {
-  return num_splits > 0 ? num_splits : (max_cache_len + kDecodeMinChunk - 1) / kDecodeMinChunk;
+// length is at least min_chunk keys.
+static int64_t decode_split_cap(int32_t max_cache_len, int32_t num_splits, int32_t min_chunk = kDecodeMinChunk) {
+  return num_splits > 0 ? num_splits : (max_cache_len + min_chunk - 1) / min_chunk;
 }
 
 // Work-group slots of the decode split kernel on the current device (2 per CU).
@@ -593,8 +593,9 @@ static int32_t decode_slots() {
   return 2 * cus;
 }
 
-static size_t decode_ws_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_keys, int32_t num_splits) {
-  const int64_t cap = decode_split_cap(max_keys, num_splits);
+static size_t decode_ws_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_keys, int32_t num_splits,
+                              int32_t min_chunk = kDecodeMinChunk) {
+  const int64_t cap = decode_split_cap(max_keys, num_splits, min_chunk);
   const size_t slots = (size_t)num_seqs * num_q_heads * cap;
   // partials, then the split plan: 2 ints + one int2 per (sequence, split) item
   return round_up(slots * kHeadDim * sizeof(float)) + round_up(slots * 2 * sizeof(float)) +
@@ -654,12 +655,14 @@ static gptoss_status decode_args(DecodeParams& p, int32_t num_seqs, int32_t num_
 // Split sizing, workspace carving and launch. eff: most keys one sequence reads
 // (the workspace was sized for ws_keys >= eff).
 static gptoss_status decode_run(DecodeParams& p, int32_t num_q_heads, int32_t eff, int32_t ws_keys,
-                                void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
-  const size_t need = decode_ws_bytes(p.num_seqs, num_q_heads, ws_keys, num_splits);
+                                void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream,
+                                int32_t min_chunk = kDecodeMinChunk) {
+  const size_t need = decode_ws_bytes(p.num_seqs, num_q_heads, ws_keys, num_splits, min_chunk);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
     return fail(GPTOSS_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                 workspace_bytes);
-  if (num_splits == 1 || (num_splits == 0 && eff <= kDecodeMinChunk)) {
+  p.min_chunk = min_chunk;
+  if (num_splits == 1 || (num_splits == 0 && eff <= min_chunk)) {
     // one split per sequence (e.g. window layers): no plan, work item = sequence
     p.direct_chunk = (eff + 127) / 128 * 128;
     p.num_splits = 1;
@@ -670,11 +673,11 @@ static gptoss_status decode_run(DecodeParams& p, int32_t num_q_heads, int32_t ef
     // planned on the device from the cache lengths: about 1.3 work items per slot
     p.chunk_fixed = 0;
     p.target_chunks = decode_slots() * 13 / 10;
-    p.num_splits = (eff + kDecodeMinChunk - 1) / kDecodeMinChunk;
+    p.num_splits = (eff + min_chunk - 1) / min_chunk;
   }
   // p.num_splits <= decode_split_cap(ws_keys): the partial buffers fit the workspace
   char* ws = static_cast<char*>(workspace);
-  const size_t cap = (size_t)p.num_seqs * num_q_heads * decode_split_cap(ws_keys, num_splits);
+  const size_t cap = (size_t)p.num_seqs * num_q_heads * decode_split_cap(ws_keys, num_splits, min_chunk);
   p.part_o = reinterpret_cast<float*>(ws);
   p.part_ml = reinterpret_cast<float*>(ws + round_up(cap * kHeadDim * sizeof(float)));
   p.plan = reinterpret_cast<int32_t*>(ws + round_up(cap * kHeadDim * sizeof(float)) + round_up(cap * 2 * sizeof(float)));
@@ -787,6 +790,61 @@ gptoss_status gptoss_attn_decode_kv(const gptoss_kv_layout* layout, int32_t num_
   }
   const int32_t keys = decode_max_keys(layout, max_seqlen, window);
   return decode_run(p, num_q_heads, keys, keys, workspace, workspace_bytes, num_splits, stream);
+}
+
+static_assert(GPTOSS_DECODE_SCRATCH_BYTES == kStaticScratchBytes, "scratch size in the header and the library");
+
+gptoss_status gptoss_attn_decode_kv_noalloc(const gptoss_kv_layout* layout, int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim, const void* q,
+                                            const int64_t q_strides[2], const void* k_cache, const void* v_cache,
+                                            const int32_t* cache_seqlens, int32_t max_seqlen, const float* sinks,
+                                            float softmax_scale, int32_t window, const void* table,
+                                            int32_t table_rows, int32_t rotary_dim, void* out,
+                                            const int64_t o_strides[2], int32_t num_splits, void* stream) {
+  DecodeParams p;
+  memset(&p, 0, sizeof p);
+  gptoss_status st = decode_args(p, num_seqs, num_q_heads, num_kv_heads, head_dim, q, q_strides, k_cache, v_cache,
+                                 cache_seqlens, max_seqlen, sinks, softmax_scale, window, table, table_rows,
+                                 rotary_dim, out, o_strides, num_splits);
+  if (st != GPTOSS_OK) return st;
+  st = check_layout(layout, max_seqlen, true, window);
+  if (st != GPTOSS_OK || num_seqs == 0) return st;
+  const int32_t keys = decode_max_keys(layout, max_seqlen, window);
+  // The partials must fit the fixed scratch: with a planned split count, the
+  // shortest split grows (a multiple of 128 keys) until the most splits a
+  // sequence can take fit; a caller-given count must fit as it is.
+  // bytes per split a sequence may take: partials (acc[64], m, l) of every query
+  // head and one plan entry; the three regions round up by at most 3 * kAlign
+  const size_t per_split = (size_t)num_seqs * num_q_heads * (kHeadDim + 2) * sizeof(float) +
+                           (size_t)num_seqs * 2 * sizeof(int32_t);
+  int32_t min_chunk = kDecodeMinChunk;
+  if (num_splits == 0 && decode_ws_bytes(num_seqs, num_q_heads, keys, 0, min_chunk) > kStaticScratchBytes) {
+    const int64_t most = (int64_t)((kStaticScratchBytes - 4 * kAlign) / per_split);
+    if (most >= 1) {
+      const int64_t c = ((keys + most - 1) / most + 127) / 128 * 128;
+      min_chunk = (int32_t)std::max<int64_t>(c, kDecodeMinChunk);
+    }
+  }
+  const size_t need = decode_ws_bytes(num_seqs, num_q_heads, keys, num_splits, min_chunk);
+  if (need > kStaticScratchBytes)
+    return fail(GPTOSS_ERR_WORKSPACE,
+                "the allocation-free decode holds at most %zu bytes of partials; this call needs %zu "
+                "(fewer sequences or splits, or gptoss_attn_decode_kv with a workspace)",
+                kStaticScratchBytes, need);
+  void* ws = nullptr;
+  st = hip_status(static_scratch(&ws), "scratch address");
+  if (st != GPTOSS_OK) return st;
+  p.kind = layout->kind;
+  p.kv_sn = layout->strides[0]; p.kv_sp = layout->strides[1]; p.kv_sh = layout->strides[2];
+  if (layout->kind == GPTOSS_CACHE_PAGED) {
+    p.page_log2 = ilog2_pow2(layout->capacity);
+    p.block_table = layout->block_table;
+    p.max_pages = layout->max_pages;
+    p.num_pages = layout->num_pages;
+  } else if (layout->kind == GPTOSS_CACHE_RING) {
+    p.ring_slots = layout->capacity;
+  }
+  return decode_run(p, num_q_heads, keys, keys, ws, kStaticScratchBytes, num_splits, stream, min_chunk);
 }
 
 gptoss_status gptoss_qkv_proj_rope(const gptoss_seq_desc* desc, const void* x, int64_t x_row_stride,

@@ -18,6 +18,8 @@
 // Combine kernel: per (sequence, query head) it merges the partials and adds
 // the sink exactly once: M = max(sigma, m_s), l = exp(sigma - M) + sum l_s
 // exp(m_s - M), o = sum acc_s exp(m_s - M) / l (all in log2 units).
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -242,8 +244,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
 // of times, a few hundred large ones leave the machine idle at the end. The
 // plan kernel reads the cache lengths and picks the split length so that the
 // call has about target_chunks (sequence, split) items: total visible keys /
-// target_chunks, rounded up to a multiple of 128, at least kDecodeMinChunk (so
-// the partial buffers sized on the host always suffice). A caller-given split
+// target_chunks, rounded up to a multiple of 128, at least min_chunk (so the
+// partial buffers sized on the host always suffice). A caller-given split
 // count is used as is. It then writes the list of items, the full-length
 // splits first and each sequence's shorter last split after them, so the split
 // kernel's work groups take real work only and the short items run last.
@@ -271,9 +273,9 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams 
     if (chunk <= 0) {
       const long long want = (part[0] + p.target_chunks - 1) / max(p.target_chunks, 1);
       long long c = (want + 127) / 128 * 128;
-      c = c < kDecodeMinChunk ? kDecodeMinChunk : c;
+      c = c < p.min_chunk ? p.min_chunk : c;
       const long long cap = ((long long)p.max_cache_len + 127) / 128 * 128;
-      chunk = (int)(c > cap ? (cap > kDecodeMinChunk ? cap : kDecodeMinChunk) : c);
+      chunk = (int)(c > cap ? (cap > p.min_chunk ? cap : p.min_chunk) : c);
     }
     chunk_s = chunk;
     p.plan[0] = chunk;
@@ -367,7 +369,37 @@ __global__ __launch_bounds__(NTC) void decode_combine_kernel(DecodeParams p) {
   }
 }
 
+// Scratch of the allocation-free decode entry point (partials and plan of one
+// call), one copy per GPU, held until the process ends. Calls that overlap on
+// one GPU share it and race; nothing in it needs to start at zero (the plan
+// kernel writes the plan, the split kernel every partial the combine reads).
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
 }  // namespace
+
+// Device address of `scratch` on the current device. In host code the array's
+// name stands for a host-side shadow, not device memory, so kernels are handed
+// this address, looked up once per device.
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;

@@ -118,6 +118,7 @@ struct DecodeParams {
   int32_t num_splits;            // split slots per (sequence, KV head) in the partial buffers
   int32_t chunk_fixed;           // > 0: keys per split given by the caller; 0: planned on the device
   int32_t target_chunks;         // planned: aim for about this many (sequence, split) work items
+  int32_t min_chunk;             // planned: fewest keys per split (a multiple of 128, >= kDecodeMinChunk)
   int32_t* plan;                 // device: keys per split, item count, then int2 (sequence, split) items
   int32_t max_items;             // work groups launched for the split kernel
   int32_t direct_chunk;          // > 0: one split of this many keys per sequence, no plan (item = sequence)
@@ -181,5 +182,11 @@ struct AppendParams {
 };
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 constexpr int kDecodeMinChunk = 512;   // smallest planned split (keys)
+
+// Scratch of the allocation-free decode entry point: a file-scope __device__
+// array of kStaticScratchBytes per GPU. static_scratch() returns its address on
+// the current device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void** ptr);
 
 }  // namespace gptoss

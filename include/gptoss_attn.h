@@ -449,6 +449,38 @@ gptoss_status gptoss_attn_decode_kv(const gptoss_kv_layout* layout, int32_t num_
                                     void* stream);
 
 /*
+ * gptoss_attn_decode_kv without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The split partials and the split plan live
+ * in a fixed scratch array the library holds on each GPU it runs on
+ * (GPTOSS_DECODE_SCRATCH_BYTES, until the process ends); this call allocates
+ * nothing and frees nothing. Its address is looked up on the first call on
+ * each device (make one call before capturing a graph on a new device).
+ * Arguments and results as for gptoss_attn_decode_kv, minus the workspace.
+ * With num_splits = 0 the shortest planned split is lengthened (in steps of
+ * 128 keys) when the partials of the default plan would not fit; the result
+ * stays within the same tolerance, and is bit-identical to
+ * gptoss_attn_decode_kv whenever the default plan fits. Calls whose partials
+ * cannot fit (num_seqs * num_q_heads * splits * 264 bytes plus the plan)
+ * return GPTOSS_ERR_WORKSPACE before any launch.
+ * All calls of one process on one GPU share that GPU's scratch and it keeps
+ * the last call's contents: calls that can run at the same time on one GPU
+ * (on different streams, or from different host threads without ordering)
+ * race and give undefined results; calls ordered on one stream do not.
+ * Nothing in it needs to start at zero (each call writes what it reads).
+ */
+#define GPTOSS_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+gptoss_status gptoss_attn_decode_kv_noalloc(const gptoss_kv_layout* layout, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                            const void* q, const int64_t q_strides[2],
+                                            const void* k_cache, const void* v_cache,
+                                            const int32_t* cache_seqlens, int32_t max_seqlen,
+                                            const float* sinks, float softmax_scale, int32_t window,
+                                            const void* table, int32_t table_rows, int32_t rotary_dim,
+                                            void* out, const int64_t o_strides[2], int32_t num_splits,
+                                            void* stream);
+
+/*
  * The q, k and v projections ahead of the attention with the RoPE applied to q
  * and k in the same kernel (the gpt-oss-20b module print-out: q_proj
  * 2880 -> Hq*64, k_proj and v_proj 2880 -> Hkv*64, Linear with bias; rope_utils

@@ -304,6 +304,31 @@ def test_decode_kv_argument_errors(lib):
     assert _decode_kv(lib, _layout(), n=0) == OK
 
 
+def _decode_noalloc(lib, lay, **kw):
+    a = dict(n=4, hq=64, hkv=8, d=64, q=P, qs=I64x2(64 * 64, 64), k=P, v=P, lens=P, maxlen=1024, sinks=P,
+             scale=0.125, window=0, table=P, rows=1024, rd=64, out=P, os=I64x2(64 * 64, 64), splits=0)
+    a.update(kw)
+    return lib.gptoss_attn_decode_kv_noalloc(ctypes.byref(lay) if lay is not None else None, a["n"], a["hq"],
+                                             a["hkv"], a["d"], a["q"], a["qs"], a["k"], a["v"], a["lens"],
+                                             a["maxlen"], a["sinks"], a["scale"], a["window"], a["table"], a["rows"],
+                                             a["rd"], a["out"], a["os"], a["splits"], None)
+
+
+def test_decode_noalloc_argument_errors(lib):
+    """The allocation-free decode checks its arguments like gptoss_attn_decode_kv and refuses,
+    before any launch, calls whose partials cannot fit its fixed 32 MiB scratch."""
+    assert _decode_noalloc(lib, None) == ERR_NULL
+    assert _decode_noalloc(lib, _layout(), d=128) == ERR_UNSUPPORTED
+    assert _decode_noalloc(lib, _layout(kind=2, cap=128), window=64) == ERR_UNSUPPORTED
+    assert _decode_noalloc(lib, _layout(), lens=None) == ERR_NULL
+    assert _decode_noalloc(lib, _layout(), n=0) == OK
+    # one split per sequence already needs 2048 * 64 * 264 bytes > 32 MiB
+    assert _decode_noalloc(lib, _layout(cap=1), n=2048, maxlen=1, rows=1) == ERR_WORKSPACE
+    assert b"32 MiB" in lib.gptoss_last_error() or b"33554432" in lib.gptoss_last_error()
+    # a caller-given split count is not shortened: 64 splits of 64 sequences need 66 MiB
+    assert _decode_noalloc(lib, _layout(cap=32768), n=64, maxlen=32768, rows=32768, splits=64) == ERR_WORKSPACE
+
+
 def test_decode_kv_workspace_size(lib):
     # contiguous == the plain decode's size; a ring is sized by its slots; a paged window
     # layer by window + 31 keys (its reads start at a 32-key boundary)
