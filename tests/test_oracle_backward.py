@@ -8,8 +8,7 @@ Each pin comes from outside oracle.backward:
     an extra logit column with a zero value row;
   * with sinks = -inf, torch's scaled_dot_product_attention backward (library);
   * lse against torch.logsumexp over [sigma, visible scores];
-  * closed forms for a single key (gradients and the rounding-noise scales the
-    GPU tests' tolerance uses);
+  * closed forms for a single key;
   * THD equals per-sequence BSHD; the gradients of GQA sum over the group.
 """
 
@@ -189,44 +188,15 @@ def test_rotate_transpose_is_the_adjoint():
     assert np.isclose((rx * y).sum(), (x * rty).sum(), rtol=1e-12)
 
 
-def test_noise_scales_single_key_closed_form():
-    """Noise scales for one key: p = e^s / (e^sigma + e^s), o = p v, dS = p (1 - p) <dO, v>,
-    E = sum_d (dO_d o_d)^2; n_dv^2 = sum_h p_h^2 dO_h^2; n_dq~^2 = tau^2 (dS^2 k^2 + E p^2 k^2);
-    n_dsigma^2 = (1 - p)^2 E; m_dsigma = |(1 - p) p <dO, v>|."""
-    rng = np.random.default_rng(8)
-    q = rng.standard_normal((1, 1, 8, 64))
-    k = rng.standard_normal((1, 1, 1, 64))
-    v = rng.standard_normal((1, 1, 1, 64))
-    dout = rng.standard_normal((1, 1, 8, 64))
-    sinks = rng.standard_normal(8)
-    n = oracle.prefill_bshd_backward(q, k, v, sinks, TAU, 0, dout, rotate_qk=False, with_noise=True)["noise"]
-    pv = np.zeros(8)
-    for h in range(8):
-        s = TAU * float(q[0, 0, h] @ k[0, 0, 0])
-        p = np.exp(s) / (np.exp(sinks[h]) + np.exp(s))
-        pv[h] = p
-        dvd = float(dout[0, 0, h] @ v[0, 0, 0])
-        E = float(((dout[0, 0, h] * p * v[0, 0, 0]) ** 2).sum())
-        ds = p * (1 - p) * dvd
-        kk = k[0, 0, 0]
-        assert np.allclose(n["dq"][0, 0, h], TAU * np.sqrt(ds ** 2 * kk ** 2 + E * p ** 2 * kk ** 2), rtol=1e-11)
-        assert np.isclose(n["dsinks"][h], (1 - p) * np.sqrt(E), rtol=1e-11)
-        assert np.isclose(n["m_dsinks"][h], abs((1 - p) * p * dvd), rtol=1e-11)
-    assert np.allclose(n["dv"][0, 0, 0], np.sqrt((pv[:, None] ** 2 * dout[0, 0] ** 2).sum(0)), rtol=1e-11)
-
-
 @pytest.mark.parametrize("window", [0, 6])
 def test_rows_equal_the_whole_problem(window):
     """prefill_backward_rows (selected query rows and a key range, sub-problems only)
     equals the matching entries of the full backward."""
     B, S, hq, hkv, d = 1, 40, 16, 2, 64
     q, k, v, sinks, dout = _inputs(B, S, hq, hkv, d, 51 + window)
-    full = oracle.prefill_bshd_backward(q, k, v, sinks, TAU, window, dout, CFG, with_noise=True)
+    full = oracle.prefill_bshd_backward(q, k, v, sinks, TAU, window, dout, CFG)
     rows = [0, 3, 17, 39]
     part = oracle.prefill_backward_rows(q[0], k[0], v[0], sinks, TAU, window, dout[0], rows, 20, 31, CFG)
     assert np.allclose(part["dq"], full["dq"][0, rows], rtol=1e-12, atol=1e-13)
     assert np.allclose(part["dk"], full["dk"][0, 20:31], rtol=1e-12, atol=1e-13)
     assert np.allclose(part["dv"], full["dv"][0, 20:31], rtol=1e-12, atol=1e-13)
-    assert np.allclose(part["noise"]["dq"], full["noise"]["dq"][0, rows], rtol=1e-12)
-    assert np.allclose(part["noise"]["dk"], full["noise"]["dk"][0, 20:31], rtol=1e-12)
-    assert np.allclose(part["noise"]["dv"], full["noise"]["dv"][0, 20:31], rtol=1e-12)
