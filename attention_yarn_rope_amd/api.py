@@ -118,7 +118,7 @@ def attn_prefill(q, k, v, sinks, window=0, table=None, softmax_scale=None, cu_se
     need = lib.gptoss_attn_prefill_workspace_size(ctypes.byref(desc))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale   # 0: the library's head_dim ** -0.5
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     if table is not None:
         _bf16(table, "table")
@@ -153,7 +153,7 @@ def attn_prefill_lse(q, k, v, sinks, window=0, table=None, softmax_scale=None, c
     need = lib.gptoss_attn_prefill_workspace_size(ctypes.byref(desc))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale   # 0: the library's head_dim ** -0.5
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     check("gptoss_attn_prefill_lse", lib.gptoss_attn_prefill_lse(
         ctypes.byref(desc), _ptr(q), _strides3(q, layout), _ptr(k), _strides3(k, layout),
@@ -191,7 +191,7 @@ def attn_prefill_backward(q, k, v, sinks, out, dout, lse, window=0, table=None, 
     need = lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(desc))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale   # 0: the library's head_dim ** -0.5
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     check("gptoss_attn_prefill_backward", lib.gptoss_attn_prefill_backward(
         ctypes.byref(desc), _ptr(q), _strides3(q, layout), _ptr(k), _strides3(k, layout),
@@ -223,7 +223,7 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, sinks, window=0, table=None,
     need = lib.gptoss_attn_decode_workspace_size(N, Hq, Lmax, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale   # 0: the library's head_dim ** -0.5
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     ks = k_cache.stride()
     check("gptoss_attn_decode", lib.gptoss_attn_decode(
@@ -320,7 +320,7 @@ def attn_decode_kv(q, k_cache, v_cache, cache_seqlens, sinks, kind="contiguous",
                                                     int(num_splits))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale   # 0: the library's head_dim ** -0.5
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     check("gptoss_attn_decode_kv", lib.gptoss_attn_decode_kv(
         ctypes.byref(lay), N, Hq, Hkv, D, _ptr(q), I64x2(q.stride(0), q.stride(1)), _ptr(k_cache), _ptr(v_cache),
@@ -347,7 +347,7 @@ def attn_decode_kv_noalloc(q, k_cache, v_cache, cache_seqlens, sinks, kind="cont
         max_seqlen = _cache_max_seqlen(kind, k_cache, block_table, table)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale   # 0: the library's head_dim ** -0.5
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     check("gptoss_attn_decode_kv_noalloc", _lib.load().gptoss_attn_decode_kv_noalloc(
         ctypes.byref(lay), N, Hq, Hkv, D, _ptr(q), I64x2(q.stride(0), q.stride(1)), _ptr(k_cache), _ptr(v_cache),
@@ -425,7 +425,7 @@ def attn_prefill_shard(q, k, v, q_offset, kv_offset, window=0, table=None, softm
     lib = _lib.load()
     if workspace is None:
         workspace = torch.empty(max(prefill_shard_workspace_size(q, k), 1), dtype=torch.uint8, device=q.device)
-    scale = D ** -0.5 if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale   # 0: the library's head_dim ** -0.5
     tptr, trows, tdim = (_ptr(table), table.shape[0], table.shape[1]) if table is not None else (None, 0, 0)
     check("gptoss_attn_prefill_shard", lib.gptoss_attn_prefill_shard(
         ctypes.byref(desc), _ptr(q), _strides3(q, _lib.BSHD), _ptr(k), _strides3(k, _lib.BSHD), _ptr(v),

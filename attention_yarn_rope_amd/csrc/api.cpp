@@ -44,6 +44,17 @@ bool strides_ok(const int64_t* s, int n) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// The scale of the scores (page "nemo_automodel.components.models.gpt_oss.layers",
+// GptOssAttention.softmax_scale = head_dim ** -0.5): 0 selects that default,
+// any other value must be finite and positive. Returns false for an invalid one.
+bool resolve_scale(float& scale, int32_t head_dim) {
+  if (scale == 0.0f) {
+    scale = 1.0f / std::sqrt((float)head_dim);   // 0.125 exactly for head_dim 64
+    return true;
+  }
+  return scale > 0.0f && std::isfinite(scale);
+}
+
 // YaRN (page "nemo_automodel.components.models.gpt_oss.rope_utils",
 // RotaryEmbedding._compute_concentration_and_inv_freq): theta_i =
 // base^(-2i/d); with s > 1 the ramp gamma_i = clamp((i - lo) / (hi - lo), 0, 1)
@@ -243,16 +254,18 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
       !strides_ok(o_strides, 3) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
   if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
-    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (!resolve_scale(softmax_scale, desc->head_dim))
+    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be 0 (head_dim^-0.5) or finite and > 0");
   // a 64-key tile of K or V must span less than 2 GiB (32-bit buffer offsets)
   if (k_strides[1] * 2 * 64 > (int64_t)INT32_MAX || v_strides[1] * 2 * 64 > (int64_t)INT32_MAX)
     return fail(GPTOSS_ERR_UNSUPPORTED, "token strides of k and v must be below 2^24 elements");
   // rows of the table the rotations read
   const int32_t need_rows = shard ? std::max(shard->q_offset + desc->seqlen, shard->kv_offset + shard->kv_len)
                                   : desc_max_len(desc);
-  st = check_table(table, table_rows, rotary_dim, need_rows);
+  st = check_table(table, table_rows, rotary_dim, need_rows, true);
   if (st != GPTOSS_OK) return st;
+  if (table && rotary_dim != kHeadDim && krot == KROT_FUSED)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "k rotation inside the tile loads needs rotary_dim 64 (got %d)", rotary_dim);
   const int32_t kv_len = shard ? shard->kv_len : desc->seqlen;   // BSHD keys per sequence
   const size_t need = prefill_ws_bytes(desc, shard ? (int64_t)desc->batch * kv_len : desc_tokens(desc));
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
@@ -278,6 +291,7 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
   p.no_sink = sinks ? 0 : 1;
   p.table = static_cast<const uint16_t*>(table);
   p.table_rows = table_rows;
+  p.rot_chunks = table ? rotary_dim / 16 : kHeadDim / 16;
   p.batch = desc->batch;
   p.seqlen = desc->seqlen;
   p.num_kv_heads = desc->num_kv_heads;
@@ -322,7 +336,7 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
     r.num_seqs = desc->batch;
     r.table = p.table;
     r.table_rows = table_rows;
-    r.rot_chunks = kHeadDim / 16;
+    r.rot_chunks = rotary_dim / 16;
     r.pos0 = p.k_pos0;
     st = hip_status(launch_rope_qk(r, s), "k rotation kernel");
     if (st != GPTOSS_OK) return st;
@@ -485,8 +499,8 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
       !aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse))
     return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
   if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
-    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (!resolve_scale(softmax_scale, desc->head_dim))
+    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be 0 (head_dim^-0.5) or finite and > 0");
   if (k_strides[1] * 2 * 64 > (int64_t)INT32_MAX || v_strides[1] * 2 * 64 > (int64_t)INT32_MAX)
     return fail(GPTOSS_ERR_UNSUPPORTED, "token strides of k and v must be below 2^24 elements");
   st = check_table(table, table_rows, rotary_dim, desc_max_len(desc));
@@ -622,8 +636,8 @@ static gptoss_status decode_args(DecodeParams& p, int32_t num_seqs, int32_t num_
   if (max_len < 1) return fail(GPTOSS_ERR_SHAPE, "the maximum cache length must be >= 1");
   if (num_splits < 0) return fail(GPTOSS_ERR_SHAPE, "num_splits must be >= 0");
   if (window < 0) return fail(GPTOSS_ERR_SHAPE, "window must be >= 0 (0 = full causal)");
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
-    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (!resolve_scale(softmax_scale, head_dim))
+    return fail(GPTOSS_ERR_SHAPE, "softmax_scale must be 0 (head_dim^-0.5) or finite and > 0");
   if (num_seqs == 0) return GPTOSS_OK;
   if (!q || !k_cache || !v_cache || !cache_seqlens || !sinks || !out || !q_strides || !o_strides)
     return fail(GPTOSS_ERR_NULL, "q, caches, cache_seqlens, sinks, out and all strides are required");
@@ -632,7 +646,7 @@ static gptoss_status decode_args(DecodeParams& p, int32_t num_seqs, int32_t num_
   if (o_strides[0] < 0 || o_strides[1] < 0 || (o_strides[0] & 1) || (o_strides[1] & 1) ||
       (reinterpret_cast<uintptr_t>(out) & 3))
     return fail(GPTOSS_ERR_UNSUPPORTED, "out must be 4-byte aligned with even strides");
-  gptoss_status st = check_table(table, table_rows, rotary_dim, max_len);
+  gptoss_status st = check_table(table, table_rows, rotary_dim, max_len, true);
   if (st != GPTOSS_OK) return st;
   p.q = static_cast<const uint16_t*>(q);
   p.q_sn = q_strides[0]; p.q_sh = q_strides[1];
@@ -647,6 +661,7 @@ static gptoss_status decode_args(DecodeParams& p, int32_t num_seqs, int32_t num_
   p.sinks = sinks;
   p.table = static_cast<const uint16_t*>(table);
   p.table_rows = table_rows;
+  p.rot_chunks = table ? rotary_dim / 16 : kHeadDim / 16;
   p.o = static_cast<uint16_t*>(out);
   p.o_sn = o_strides[0]; p.o_sh = o_strides[1];
   return GPTOSS_OK;

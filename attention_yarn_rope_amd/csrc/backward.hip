@@ -24,15 +24,19 @@
 //                      dP sums start from -D, so dP - D needs no subtraction.
 //   bwd_sink_kernel    dsigma per head: one work group per head sums its rows
 //                      in a fixed order (no atomics, reproducible).
-//   bwd_kv_kernel      work item (sequence, KV head, 64 keys), 4 waves: wave w
-//                      holds K and V of 32 of the keys as MFMA fragments and
-//                      takes 4 of the 8 query heads; it walks every 32-query
-//                      block that can see its keys: S = Q K^T and dP = dO V^T
-//                      (8 + 8 MFMAs), P and dS in registers, then
-//                      dV^T += dO^T P and dK^T += Q^T dS (8 + 8 MFMAs; dO^T
-//                      and Q^T through a per-wave LDS tile and transpose
-//                      reads). The two waves of each 32 keys are summed
-//                      through LDS at the end.
+//   bwd_kv_kernel      work item (sequence, KV head, 128 keys), 4 waves: wave w
+//                      holds K and V of its own 32 keys as MFMA fragments and
+//                      fp32 dK^T, dV^T for them over all 8 query heads of the
+//                      group, so no sum across waves is needed. The waves walk
+//                      every 32-query block that can see the keys, from the last
+//                      one down, one query head at a time: S = Q K^T and
+//                      dP = dO V^T - D (8 + 8 MFMAs, q and dO rows as A operands
+//                      from LDS), P and dS in registers, then dV^T += dO^T P and
+//                      dK^T += Q^T dS (8 + 8 MFMAs, dO^T and Q^T by transpose
+//                      reads). Each step's 32 q and dO rows and their (lse, -D)
+//                      words are fetched by the 4 waves together, a quarter each,
+//                      during the step before, into the other half of a
+//                      double-buffered LDS tile: one barrier per step.
 // dq, dk, dv are written once each (no atomics), rounded to bf16 from fp32.
 #include "common.h"
 #include "internal.h"

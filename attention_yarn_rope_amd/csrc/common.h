@@ -205,6 +205,29 @@ __device__ __forceinline__ int32_t find_seq(const int32_t* cu, int32_t num_seqs,
   return lo;
 }
 
+// Chunk c (dims 8c .. 8c + 7, already loaded as xc) of a row rotated with
+// rotary_dim = 16 hb (rope_utils page, apply_rotary_emb: the first rotary_dim
+// dims rotate in half-split pairs (i, i + rotary_dim / 2), the rest pass
+// through). A chunk below hb pairs with chunk c + hb (its y1 = x1 C - x2 S), a
+// chunk in [hb, 2 hb) with chunk c - hb (its y2 = x2 C + x1 S), chunks at or
+// past 2 hb are returned as they are. row points at the row, tab at its table
+// row (the cos of the 8 hb pairs, then their sin). Rounded exactly like rope8.
+__device__ __forceinline__ uint4 rope_chunk_partial(const bf16_t* row, const bf16_t* tab, int c, int hb,
+                                                    const uint4& xc) {
+  if (c >= 2 * hb) return xc;
+  const bool first = c < hb;
+  const int pair = first ? c : c - hb;
+  const uint4 partner = ldg16(row + 8 * (first ? c + hb : c - hb));
+  const uint4 cs = ldg16(tab + 8 * pair), sn = ldg16(tab + 8 * (hb + pair));
+  uint4 y1, y2;
+  if (first) {
+    rope8(xc, partner, cs, sn, y1, y2);
+    return y1;
+  }
+  rope8(partner, xc, cs, sn, y1, y2);
+  return y2;
+}
+
 // Rotation of one 64-dim row by a table row (cos of the rotary_dim / 2 pairs,
 // then their sin), for the 8-dim chunks c and c + 4 a thread owns. Chunk c <
 // hb (hb = rotary_dim / 16) is rotated together with chunk c + hb, its pair

@@ -144,8 +144,13 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
     const uint4 x1 = ldg16(qp + 8 * grp), x2 = ldg16(qp + 32 + 8 * grp);
     uint4 y1 = x1, y2 = x2;
     if (ROTQ) {
-      const bf16_t* tp = p.table + (int64_t)min(max(L - 1, 0), p.table_rows - 1) * kHeadDim + 8 * grp;
-      rope8(x1, x2, ldg16(tp), ldg16(tp + 32), y1, y2);
+      const bf16_t* tp = p.table + (int64_t)min(max(L - 1, 0), p.table_rows - 1) * (16 * p.rot_chunks);
+      if (p.rot_chunks == kHeadDim / 16) {
+        rope8(x1, x2, ldg16(tp + 8 * grp), ldg16(tp + 32 + 8 * grp), y1, y2);
+      } else {   // partial rotary: each chunk with its pair partner
+        y1 = rope_chunk_partial(qp, tp, grp, p.rot_chunks, x1);
+        y2 = rope_chunk_partial(qp, tp, grp + 4, p.rot_chunks, x2);
+      }
     }
     const uint4 zero = make_uint4(0, 0, 0, 0);
     qf[0] = as_bf16x8(col < kGroup ? y1 : zero);

@@ -45,6 +45,7 @@ struct PrefillParams {
   int32_t no_sink;               // 1: no sink term (the sinks are loaded and ignored)
   const uint16_t* table;         // NULL: q (and k) already rotated
   int32_t table_rows;
+  int32_t rot_chunks;            // rotary_dim / 16: 4 rotates all 64 dims, 1..3 the first 16, 32, 48
   int32_t batch;                 // BSHD batch, or number of THD sequences
   int32_t seqlen;                // BSHD S, or THD total tokens
   int32_t num_kv_heads;
@@ -115,6 +116,7 @@ struct DecodeParams {
   const float* sinks;
   const uint16_t* table;
   int32_t table_rows;
+  int32_t rot_chunks;            // rotary_dim / 16 (4: all 64 dims)
   int32_t num_splits;            // split slots per (sequence, KV head) in the partial buffers
   int32_t chunk_fixed;           // > 0: keys per split given by the caller; 0: planned on the device
   int32_t target_chunks;         // planned: aim for about this many (sequence, split) work items

@@ -209,10 +209,15 @@ void prefill_kernel(PrefillParams p) {
     const bf16_t* qp = p.q + bb_off_q + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh;
     qx[cb][0] = ldg16(qp + 8 * grp);
     qx[cb][1] = ldg16(qp + 32 + 8 * grp);
-    if (ROTQ) {
+    if (ROTQ && p.rot_chunks == kHeadDim / 16) {
       const bf16_t* tp = p.table + (int64_t)min(pos + p.q_pos0, p.table_rows - 1) * kHeadDim + 8 * grp;
       qt[cb][0] = ldg16(tp);
       qt[cb][1] = ldg16(tp + 32);
+    } else if (ROTQ) {
+      // partial rotary: each of the lane's two chunks with its pair partner (prologue only)
+      const bf16_t* tp = p.table + (int64_t)min(pos + p.q_pos0, p.table_rows - 1) * (16 * p.rot_chunks);
+      qx[cb][0] = rope_chunk_partial(qp, tp, grp, p.rot_chunks, qx[cb][0]);
+      qx[cb][1] = rope_chunk_partial(qp, tp, grp + 4, p.rot_chunks, qx[cb][1]);
     }
     sink_raw[cb] = __ldg(p.sinks + head);
   }
@@ -222,7 +227,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     uint4 y1 = qx[cb][0], y2 = qx[cb][1];
-    if (ROTQ) rope8(qx[cb][0], qx[cb][1], qt[cb][0], qt[cb][1], y1, y2);
+    if (ROTQ && p.rot_chunks == kHeadDim / 16) rope8(qx[cb][0], qx[cb][1], qt[cb][0], qt[cb][1], y1, y2);
     qf[cb][0] = as_bf16x8(y1);
     qf[cb][1] = as_bf16x8(y2);
     // reference = the sink logit (log2 units); the sink term exp2(sigma - ref) = 1
@@ -281,12 +286,12 @@ void prefill_kernel(PrefillParams p) {
       const bf16_t* krow = kt + (kb * 16 + col) * KS + 8 * grp;
       const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(krow));
       const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32));
+      // the CB first halves, then the CB second halves accumulating in place: each
+      // dependent MFMA issues CB - 1 independent ones after the one it waits for
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        z = mfma16(a0, qf[cb][0], z);
-        sacc[kb][cb] = mfma16(a1, qf[cb][1], z);
-      }
+      for (int cb = 0; cb < CB; ++cb) sacc[kb][cb] = mfma16(a0, qf[cb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) sacc[kb][cb] = mfma16(a1, qf[cb][1], sacc[kb][cb]);
     }
 
     // ---- mask: only steps that are not fully visible to every query of the item.

@@ -30,11 +30,12 @@
  *     outside the buffers described by the host-side sizes.
  *
  * Supported now: head_dim == 64, num_q_heads == 8 * num_kv_heads (the GPT-OSS
- * grouping: 64 query heads over 8 KV heads). rotary_dim is 64 for the
- * attention entry points that take a table; gptoss_rope_qk and
- * gptoss_kv_append also rotate a partial rotary_dim of 16, 32 or 48 (the dims
- * past it copied), after which attention runs on the pre-rotated q and k with
- * table = NULL. Other shapes return GPTOSS_ERR_UNSUPPORTED.
+ * grouping: 64 query heads over 8 KV heads). Every call that takes a table
+ * rotates rotary_dim = 16, 32, 48 or 64 dims (partial rotary, rope_utils page,
+ * apply_rotary_emb: the dims past rotary_dim pass through), except the
+ * backward pass, the k rotation inside the prefill tile loads
+ * (GPTOSS_KROT_FUSED) and the projection epilogue, which take 64 (the
+ * projection also 32). Other shapes return GPTOSS_ERR_UNSUPPORTED.
  */
 #ifndef GPTOSS_ATTN_H
 #define GPTOSS_ATTN_H
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define GPTOSS_ABI_VERSION 5
+#define GPTOSS_ABI_VERSION 6
 
 typedef enum {
   GPTOSS_OK = 0,
@@ -163,11 +164,17 @@ gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc,
  *  denominator).
  *   q, k, v: bf16 in the desc's layout (strides as in gptoss_rope_qk).
  *            With a table, q and k are the UN-rotated projections and are
- *            rotated on the fly, bit-identically to gptoss_rope_qk; with
+ *            rotated on the fly, bit-identically to gptoss_rope_qk with the
+ *            same table (rotary_dim 16, 32, 48 or 64: the table's width); with
  *            table == NULL they are taken as already rotated.
+ *   sinks -INFINITY (or a shard, which has no sink term) gives the plain
+ *            softmax over the visible keys for any logits: such a row's
+ *            reference is its own largest score, so rows whose logits all
+ *            lie far below zero do not underflow.
  *   sinks:   device fp32 [num_q_heads]; sink logit of each query head, in the
  *            units of the scaled scores (-INFINITY disables it).
- *   softmax_scale: tau (0.125 for head_dim 64).
+ *   softmax_scale: tau; 0 selects head_dim ** -0.5 (0.125 for head_dim 64),
+ *           any other value must be finite and > 0 (else GPTOSS_ERR_SHAPE).
  *   window:  0 = full causal; W > 0: key j is visible to query i iff
  *            0 <= i - j < W (W = 128 counts the query itself).
  *   out:     bf16, same layout as q, o_strides like q_strides.

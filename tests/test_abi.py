@@ -2,7 +2,10 @@
 computes the host-side YaRN parameters exactly like the oracle, and rejects bad
 arguments with the documented status codes before launching anything.
 
-No call here reaches a kernel launch (each returns on argument checks first).
+No call here reaches a kernel launch (each returns on argument checks first):
+the argument checks pass fake device pointers, so they are skipped where a GPU
+is visible, and every call's status is checked against GPTOSS_ERR_HIP (what a
+launch attempt returns on a host without a GPU).
 """
 
 import ctypes
@@ -19,15 +22,53 @@ from attention_yarn_rope_amd._lib import I64x2, I64x3, KVLayout, RopeConfig, Seq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gptoss_attn.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE = 0, 1, 2, 3, 4
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4, 5
 
 
-@pytest.fixture(scope="module")
-def lib():
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+class _NoLaunch:
+    """The library with every status-returning call checked: GPTOSS_ERR_HIP means the call got
+    past its argument checks to a kernel launch, which a fake-pointer check must never do."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        fn = getattr(self._lib, name)
+        if not name.startswith("gptoss_") or fn.restype is not ctypes.c_int:
+            return fn
+
+        def call(*args):
+            st = fn(*args)
+            assert st != ERR_HIP, f"{name} got past its argument checks to a kernel launch"
+            return st
+        return call
+
+
+def _load():
     if not os.path.exists(_lib.LIB_PATH):
         from attention_yarn_rope_amd import build
         build.build(verbose=False)
     return _lib.load()
+
+
+@pytest.fixture(scope="module")
+def real_lib():
+    return _load()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if _gpu_visible():
+        pytest.skip("argument checks with fake device pointers run on a host without a GPU")
+    return _NoLaunch(_load())
 
 
 def _declared_functions():
@@ -36,19 +77,19 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(gptoss_[a-z0-9_]+)\s*\(", text)))
 
 
-def test_exports_every_declared_symbol(lib):
+def test_exports_every_declared_symbol(real_lib):
     names = _declared_functions()
     assert len(names) >= 10
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in gptoss_attn.h but not exported"
+        assert hasattr(real_lib, n), f"{n} declared in gptoss_attn.h but not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
 
 
-def test_abi_version_and_strings(lib):
-    assert lib.gptoss_abi_version() == 5
+def test_abi_version_and_strings(real_lib):
+    assert real_lib.gptoss_abi_version() == 6
     for code in range(6):
-        assert lib.gptoss_status_string(code)
-    assert lib.gptoss_status_string(99) == b"unknown status"
+        assert real_lib.gptoss_status_string(code)
+    assert real_lib.gptoss_status_string(99) == b"unknown status"
 
 
 def _cfg(**kw):
@@ -118,7 +159,9 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, d, q=None) == ERR_NULL
     assert _prefill(lib, d, window=-1) == ERR_SHAPE
     assert _prefill(lib, d, scale=float("nan")) == ERR_SHAPE
-    assert _prefill(lib, d, rd=32) == ERR_UNSUPPORTED
+    assert _prefill(lib, d, scale=-0.125) == ERR_SHAPE
+    assert _prefill(lib, d, scale=0.0, wsb=16) == ERR_WORKSPACE     # 0 = head_dim ** -0.5: passes the check
+    assert _prefill(lib, d, rd=24) == ERR_UNSUPPORTED             # not a multiple of 16
     assert _prefill(lib, d, rows=100) == ERR_SHAPE               # table shorter than the sequence
     assert _prefill(lib, d, qs=I64x3(128 * 64 * 64, 64 * 64, 65)) == ERR_UNSUPPORTED   # misaligned stride
     assert _prefill(lib, d, q=ctypes.c_void_p(0x10002)) == ERR_UNSUPPORTED             # misaligned pointer
@@ -181,10 +224,16 @@ def test_rope_qk_argument_errors(lib):
         assert f(ctypes.byref(d), P, S3, P, K3, P, P, P, 4096, rd, None) == ERR_UNSUPPORTED
 
 
-def test_attention_needs_full_rotary_with_a_table(lib):
-    # rotary_dim < 64 is served by gptoss_rope_qk + table = NULL, not by the attention kernels
-    assert _prefill(lib, _desc_bshd(), rd=32) == ERR_UNSUPPORTED
-    assert _decode(lib, rd=32) == ERR_UNSUPPORTED
+def test_attention_rotary_dims(lib):
+    # the attention calls rotate 16, 32, 48 or 64 dims; other widths are refused before any launch
+    assert _prefill(lib, _desc_bshd(), rd=24) == ERR_UNSUPPORTED
+    assert _prefill(lib, _desc_bshd(), rd=80) == ERR_UNSUPPORTED
+    assert _decode(lib, rd=8) == ERR_UNSUPPORTED
+    # 32 passes the table check (the call then stops at the too-small workspace)
+    assert _prefill(lib, _desc_bshd(), rd=32, wsb=16) == ERR_WORKSPACE
+    assert _decode(lib, rd=32, wsb=16) == ERR_WORKSPACE
+    # the gradients rotate back all 64 dims only
+    assert _backward(lib, _desc_bshd(), rd=32) == ERR_UNSUPPORTED
 
 
 def test_prefill_ex_rejects_unknown_k_rotation(lib):
@@ -217,7 +266,9 @@ def test_backward_argument_errors(lib):
     assert _backward(lib, d, dout=None) == ERR_NULL
     assert _backward(lib, d, lse=None) == ERR_NULL
     assert _backward(lib, d, window=-1) == ERR_SHAPE
-    assert _backward(lib, d, scale=0.0) == ERR_SHAPE
+    assert _backward(lib, d, scale=-0.125) == ERR_SHAPE
+    assert _backward(lib, d, scale=float("inf")) == ERR_SHAPE
+    assert _backward(lib, d, scale=0.0, wsb=16) == ERR_WORKSPACE     # 0 = head_dim ** -0.5: passes the check
     assert _backward(lib, d, rows=100) == ERR_SHAPE                     # table shorter than the sequence
     assert _backward(lib, d, dos=I64x3(128 * 64 * 64, 64 * 64, 65)) == ERR_UNSUPPORTED
     assert _backward(lib, d, lse=ctypes.c_void_p(0x10004)) == ERR_UNSUPPORTED

@@ -143,6 +143,20 @@ def test_sink_minus_inf_and_large(table):
             assert_close(_run_bshd(inp, w, table), _ref_bshd(inp, w), f"special sinks W={w}")
 
 
+def test_explicit_and_default_scale(table):
+    """softmax_scale = 0 (the binding's default) is head_dim ** -0.5 inside the library; an
+    explicit scale is used as given."""
+    inp = wl.prefill_bshd(1, 150, seed=18)
+    q, k, v, s = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda()
+    say("[gpu] prefill softmax_scale default and 0.2")
+    assert torch.equal(gx.attn_prefill(q, k, v, s, table=table), gx.attn_prefill(q, k, v, s, table=table,
+                                                                               softmax_scale=0.125))
+    for w in (0, 128):
+        out = gx.attn_prefill(q, k, v, s, window=w, table=table, softmax_scale=0.2)
+        ref = oracle.prefill_bshd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.sinks), 0.2, w, CFG)
+        assert_close(out, ref, f"scale 0.2 W={w}")
+
+
 def test_strided_inputs_and_output(table):
     """q/k/v as views of one fused qkv buffer; output written into a strided view."""
     g = torch.Generator().manual_seed(16)
