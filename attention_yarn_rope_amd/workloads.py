@@ -238,6 +238,15 @@ def long_context(seed=3):
     return prefill_bshd(1, 131072, seed, name="long_B1_S131072")
 
 
+def long_context_rows():
+    """The 512 sampled query rows of the 131072-token sequence: 0, 1, 127, 128, 131071
+    and the first 507 other entries of torch.randperm(131072) after manual_seed(5), sorted."""
+    special = [0, 1, 127, 128, 131071]
+    perm = torch.randperm(131072, generator=torch.Generator().manual_seed(5)).tolist()
+    extra = [r for r in perm if r not in special][:507]
+    return sorted(special + extra)
+
+
 def decode64(seed=4):
     return decode(64, 1024, 32768, seed, max_len=32768, name="decode_64seq")
 

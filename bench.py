@@ -14,10 +14,18 @@ ring caches for the window layer, and the cache append, under "decode.kv_cache".
 
 Timing uses HIP events recorded on the stream the library launches on, around
 every call inside the timed region; the whole region is bracketed by device
-synchronisation. Every section runs W untimed warm-up iterations first (default
-100): from idle, this GPU needs a few tens of milliseconds of sustained load
-before its clock settles, and calls timed earlier run up to 20 % slower. The CPU baseline is the fp64 oracle on a time-bounded sample
-of query rows of the same workload, on this host's cores.
+synchronisation. Before its timed calls every section runs its own calls for
+--settle-seconds (default 0.3 s) and then W untimed warm-up iterations: from
+idle, this GPU needs a few tens of milliseconds of sustained load before its
+clock settles, and calls timed earlier run up to 20 % slower. The timed work is
+the same either way; the JSON states the settle time. The window-layer decode
+(a 17.8 MB working set, inside the 256 MB last-level cache) has a 512 MiB buffer
+written between its timed calls, outside the timed events, so its rate is not
+served from that cache. A 1 GiB device copy is timed as well, so that HBM rates
+can be read against achievable as well as against the 8 TB/s of the data sheet.
+The CPU baseline is the fp64 oracle on time-bounded samples of every workload
+(query rows of each prefill config and layer, whole sequences of the decode),
+on this host's cores.
 
 The same two layers over 16 packed THD sequences (lengths uniform in [128, 8192])
 and over one 131072-token sequence are timed under "prefill_thd_and_long".
@@ -41,6 +49,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -131,8 +140,60 @@ def settle_clock(torch, dev, seconds):
         torch.cuda.synchronize()
 
 
-def cpu_baseline(inp, budget_s):
-    """The oracle, as it stands, on seeded query rows of the dense workload (batch 0)."""
+def settle(torch, fns, warmup, seconds):
+    """Untimed: the section's own calls for `seconds` (the clock settles under sustained load),
+    then `warmup` more rounds of them."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for fn in fns:
+            fn()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+
+
+def host_cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class _RowsF64:
+    """Indexable view of a CPU bf16 tensor that converts only the indexed rows to fp64."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        import numpy as np
+        import torch
+        return self.t[torch.as_tensor(np.asarray(idx))].double().numpy()
+
+
+def cpu_baseline(samples, budget_s):
+    """The oracle, as it stands, timed on bounded samples of every workload on the host's cores.
+
+    samples: (config, layer, kind, data). kind "rows": data = (q, k, v, sinks, window, rows) for one
+    sequence, rows in the order they are taken, a few at a time, until the entry's share of budget_s
+    is spent; kind "decode": data = (q, k_cache, v_cache, lengths, sinks, window), whole sequences in
+    order. Returns the aggregate rate and, per (config, layer), rows or sequences done, seconds and
+    GFLOP/s on unmasked FLOPs (4 * 64 * 64 per visible (query, key) pair and head)."""
     import numpy as np
     import oracle
     try:
@@ -140,26 +201,41 @@ def cpu_baseline(inp, budget_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
     except Exception:
         cores = os.cpu_count()
-    S = inp.q.shape[1]
-    q = inp.q[0].double().numpy()
-    k = inp.k[0].double().numpy()
-    v = inp.v[0].double().numpy()
-    sinks = inp.sinks.double().numpy()
-    rng = np.random.default_rng(2024)
-    order = rng.permutation(S)
-    flops, rows_done, t0 = 0, 0, time.perf_counter()
-    chunk = 32
-    while time.perf_counter() - t0 < budget_s and rows_done < S:
-        rows = np.sort(order[rows_done:rows_done + chunk])
-        for w in (0, WINDOW):
-            oracle.prefill_rows(q, k, v, sinks, 0.125, w, rows)
-            flops += sum(4 * 64 * 64 * (min(int(r) + 1, w) if w else int(r) + 1) for r in rows)
-        rows_done += len(rows)
-    secs = time.perf_counter() - t0
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": round(secs, 2),
-            "sample": f"{rows_done} seeded query rows x 64 heads of batch 0 of the dense B=4 S=4096 workload, "
-                      f"full-causal and window-128 layers, fp64 numpy on the host CPU"}
+    per = budget_s / max(len(samples), 1)
+    flops_all, secs_all, table = 0, 0.0, {}
+    for config, layer, kind, data in samples:
+        flops, done, t0 = 0, 0, time.perf_counter()
+        if kind == "rows":
+            q, k, v, sinks, w, rows = data
+            step = 1 if (w == 0 and len(rows) <= 512 and q.shape[0] > 8192) else 8
+            while done < len(rows) and time.perf_counter() - t0 < per:
+                rs = np.sort(np.asarray(rows[done:done + step]))
+                oracle.prefill_rows(q, k, v, sinks, 0.125, w, rs)
+                flops += sum(4 * 64 * 64 * (min(int(r) + 1, w) if w else int(r) + 1) for r in rs)
+                done += len(rs)
+            unit = "query rows x 64 heads"
+        else:
+            q, kc, vc, lengths, sinks, w = data
+            while done < len(lengths) and time.perf_counter() - t0 < per:
+                L = int(lengths[done])
+                lo = 0 if w <= 0 else max(0, L - w)
+                oracle.decode(q[done:done + 1].double().numpy(), kc[done:done + 1, :L].double().numpy(),
+                              vc[done:done + 1, :L].double().numpy(), [L], sinks, 0.125, w)
+                flops += 4 * 64 * 64 * (L - lo)
+                done += 1
+            unit = "sequences x 64 heads"
+        secs = time.perf_counter() - t0
+        flops_all += flops
+        secs_all += secs
+        table.setdefault(config, {})[layer] = {"done": done, "of": unit, "seconds": round(secs, 2),
+                                               "GFLOP/s": round(flops / secs / 1e9, 2) if secs > 0 else None}
+    return {"value": flops_all / secs_all / 1e12 if secs_all > 0 else None, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "cpu_model": host_cpu_model(), "seconds": round(secs_all, 2),
+            "sample": "seeded query rows of each prefill workload (tiny, dense B=4 S=4096 batch 0, the longest "
+                      "THD sequence, the 512 sampled rows of the 131072-token sequence) and whole sequences of "
+                      "the 64-sequence decode, full-causal and window-128 layers, each for an equal share of "
+                      f"{budget_s:.0f} s; fp64 numpy on the host CPU",
+            "per_config": table}
 
 
 def kv_cache_calls(torch, gx, wl, dev, dq, kc, vc, lens, dsinks, dtable, lengths, d_out, pk, pv):
@@ -209,15 +285,14 @@ def kv_cache_calls(torch, gx, wl, dev, dq, kc, vc, lens, dsinks, dtable, lengths
     }
 
 
-def kv_cache_bench(torch, wl, kvc, args, lengths, b_full, b_win):
+def kv_cache_bench(torch, wl, kvc, args, lengths, b_full, b_win, flush):
     timer = Timer(torch)
     names = ("paged_full", "ring_window", "append_1", "append_prompt")
-    for _ in range(args.warmup):
-        for n in names:
-            kvc[n]()
-    torch.cuda.synchronize()
+    settle(torch, [kvc[n] for n in names], args.warmup, args.settle_seconds)
     for _ in range(args.steps):
         for n in names:
+            if n == "ring_window":
+                flush()   # the rings (16.8 MB) would otherwise stay in the last-level cache
             timer.run(n, kvc[n])
     torch.cuda.synchronize()
     ms = {n: timer.mean_ms(n) for n in names}
@@ -236,9 +311,7 @@ def kv_cache_bench(torch, wl, kvc, args, lengths, b_full, b_win):
         step()
     step_ms = {}
     for nm, fn in (("eager", step), ("graph", graph.replay)):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        settle(torch, [fn], args.warmup, args.settle_seconds)
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record(torch.cuda.current_stream())
@@ -258,7 +331,8 @@ def kv_cache_bench(torch, wl, kvc, args, lengths, b_full, b_win):
                              "GB/s": round(b_full / (ms["paged_full"] * 1e-3) / 1e9, 1),
                              "frac_hbm_peak": round(b_full / (ms["paged_full"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "ring_window_layer": {"ms": round(ms["ring_window"], 4),
-                              "GB/s": round(b_win / (ms["ring_window"] * 1e-3) / 1e9, 1)},
+                              "GB/s": round(b_win / (ms["ring_window"] * 1e-3) / 1e9, 1),
+                              "cache": "a 512 MiB buffer written before each timed call"},
         "append_1_token_ms": round(ms["append_1"], 4),
         "decode_step": {"what": "append 1 token x 64 sequences (pool and rings) + paged full-layer decode + ring "
                                 "window-layer decode, K steps back to back",
@@ -275,8 +349,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--settle", type=float, default=0.2,
                     help="--profile modes: seconds of matrix-core load before the profiled calls")
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="seconds each timed section runs its own calls before its warm-up and timed calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--k-rotation", default="auto", choices=["auto", "fused", "separate"])
     ap.add_argument("--no-backward", action="store_true")
@@ -313,6 +389,29 @@ def main():
         torch.cuda.synchronize()
         log(f"copy: {args.steps} x 1 GiB")
         return
+
+    cpu_samples = []   # (config, layer, kind, data) for the oracle baseline at the end
+    flush_buf = None
+    copy_gbs = fill_gbs = None
+
+    def flush():
+        flush_buf.fill_(1)
+
+    if args.profile is None:
+        # achievable HBM bandwidth: a plain 1 GiB device-to-device copy (2 GiB moved per call)
+        csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        settle(torch, [lambda: cdst.copy_(csrc)], 3, args.settle_seconds)
+        timer = Timer(torch)
+        for _ in range(10):
+            timer.run("copy", lambda: cdst.copy_(csrc))
+            timer.run("fill", lambda: cdst.fill_(1))
+        torch.cuda.synchronize()
+        copy_gbs = 2 * (1 << 30) / (timer.mean_ms("copy") * 1e-3) / 1e9
+        fill_gbs = (1 << 30) / (timer.mean_ms("fill") * 1e-3) / 1e9
+        del csrc, cdst, timer
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        log(f"[bench] device copy {copy_gbs:.0f} GB/s, fill {fill_gbs:.0f} GB/s")
 
     # ---------------- prefill (the step) ----------------
     log("[bench] generating dense B=4 S=4096 workload")
@@ -443,11 +542,7 @@ def main():
 
     if args.profile is None:
         timer = Timer(torch)
-        for _ in range(args.warmup):
-            gx.rope_table(S, out=table)
-            call_full()
-            call_win()
-        torch.cuda.synchronize()
+        settle(torch, [lambda: gx.rope_table(S, out=table), call_full, call_win], args.warmup, args.settle_seconds)
         t0 = time.perf_counter()
         for _ in range(args.steps):
             timer.run("table", lambda: gx.rope_table(S, out=table))
@@ -478,9 +573,7 @@ def main():
                      for w in (0, WINDOW)}
         timer = Timer(torch)
         for w, fn in thd_calls.items():
-            for _ in range(args.warmup):
-                fn()
-            torch.cuda.synchronize()
+            settle(torch, [fn], args.warmup, args.settle_seconds)
             for _ in range(args.steps):
                 timer.run(w, fn)
             torch.cuda.synchronize()
@@ -491,8 +584,20 @@ def main():
             fl = wl.prefill_flops(ti.lengths, w)
             other_obj["thd"][nm] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1), "flops": fl}
         del tq, tk, tv, tout, tws, thd_calls, timer
+        n_long_seq = max(range(len(ti.lengths)), key=lambda n: ti.lengths[n])
+        a, b = int(ti.cu_seqlens[n_long_seq]), int(ti.cu_seqlens[n_long_seq + 1])
+        trows = __import__("numpy").random.default_rng(2025).permutation(b - a)
+        for w, nm in ((0, "full"), (WINDOW, "window128")):
+            cpu_samples.append(("thd_longest_sequence", nm, "rows", (
+                ti.q[a:b].double().numpy(), ti.k[a:b].double().numpy(), ti.v[a:b].double().numpy(),
+                ti.sinks.double().numpy(), w, trows)))
+        del ti
         li = wl.long_context()
         lq, lk, lv, lsk = (t.to(dev) for t in (li.q, li.k, li.v, li.sinks))
+        lrows = [int(r) for r in __import__("numpy").random.default_rng(2026).permutation(wl.long_context_rows())]
+        for w, nm in ((0, "full"), (WINDOW, "window128")):
+            cpu_samples.append(("long_S131072_512_rows", nm, "rows", (
+                _RowsF64(li.q[0]), _RowsF64(li.k[0]), _RowsF64(li.v[0]), li.sinks.double().numpy(), w, lrows)))
         del li
         ltab = gx.rope_table(lq.shape[1])
         lout = torch.empty_like(lq)
@@ -501,9 +606,8 @@ def main():
         n_long = max(min(args.steps, 3), 1)
         for w in (0, WINDOW):
             fn = (lambda w=w: gx.attn_prefill(lq, lk, lv, lsk, window=w, table=ltab, out=lout, workspace=lws))
-            for _ in range(2 if w == 0 else args.warmup):   # a full-layer call is ~0.15 s of load by itself
-                fn()
-            torch.cuda.synchronize()
+            # a full-layer call is ~0.13 s of load by itself: two calls settle the clock
+            settle(torch, [fn], 2 if w == 0 else args.warmup, 0.0 if w == 0 else args.settle_seconds)
             for _ in range(n_long):
                 timer.run(w, fn)
             torch.cuda.synchronize()
@@ -525,9 +629,7 @@ def main():
         # each call type in its own block of K calls after its warm-up (interleaving the three
         # measured the first one up to 20 % slower than the same kernel run back to back)
         for n in names:
-            for _ in range(args.warmup):
-                pc[n]()
-            torch.cuda.synchronize()
+            settle(torch, [pc[n]], args.warmup, args.settle_seconds)
             for _ in range(args.steps):
                 timer.run(n, pc[n])
             torch.cuda.synchronize()
@@ -552,10 +654,7 @@ def main():
         cc = cp_calls()
         timer = Timer(torch)
         names = ("offdiag", "diag", "merge")
-        for _ in range(args.warmup):
-            for nm in names:
-                cc[nm]()
-        torch.cuda.synchronize()
+        settle(torch, [cc[nm] for nm in names], max(args.warmup // 10, 1), args.settle_seconds)
         for _ in range(max(args.steps // 4, 3)):
             for nm in names:
                 timer.run(nm, cc[nm])
@@ -583,10 +682,7 @@ def main():
     if args.profile is None and not args.no_backward:
         calls = backward_calls()
         timer = Timer(torch)
-        for _ in range(args.warmup):
-            for fn in calls.values():
-                fn()
-        torch.cuda.synchronize()
+        settle(torch, list(calls.values()), args.warmup, args.settle_seconds)
         for _ in range(args.steps):
             for name, fn in calls.items():
                 timer.run(name, fn)
@@ -616,7 +712,9 @@ def main():
         vc = dinp.v_cache.to(dev)
         lens = dinp.cache_seqlens.to(dev)
         dsinks = dinp.sinks.to(dev)
-        del dinp.k_cache, dinp.v_cache
+        for w, nm in ((0, "full"), (WINDOW, "window128")):
+            cpu_samples.append(("decode_64seq", nm, "decode", (dinp.q, dinp.k_cache, dinp.v_cache, dinp.lengths,
+                                                               dinp.sinks.double().numpy(), w)))
         dtable = gx.rope_table(kc.shape[1])
         d_out = torch.empty_like(dq)
         dws = torch.empty(gx.decode_workspace_size(dq.shape[0], 64, kc.shape[1]), dtype=torch.uint8, device=dev)
@@ -642,12 +740,10 @@ def main():
             log(f"{args.profile}: {args.steps} launches")
             return
         timer = Timer(torch)
-        for _ in range(args.warmup):
-            dec(0)()
-            dec(WINDOW)()
-        torch.cuda.synchronize()
+        settle(torch, [dec(0), dec(WINDOW)], args.warmup, args.settle_seconds)
         for _ in range(args.steps):
             timer.run("dfull", dec(0))
+            flush()   # the window layer's 17.8 MB of rows would otherwise be served from the last-level cache
             timer.run("dwin", dec(WINDOW))
         torch.cuda.synchronize()
         ms_df, ms_dw = timer.mean_ms("dfull"), timer.mean_ms("dwin")
@@ -661,10 +757,12 @@ def main():
             "ms_full_layer": round(ms_df, 4), "ms_window_layer": round(ms_dw, 4),
             "bytes_full_layer": b_full, "bytes_window_layer": b_win,
             "window_layer_GBps": round(b_win / (ms_dw * 1e-3) / 1e9, 1),
+            "window_layer_cache": "a 512 MiB buffer written before each timed call",
+            "frac_of_copy": round(gbs / copy_gbs, 4) if copy_gbs else None,
             "traffic": counters_traffic("decode_full_64seq", "decode"),
         }
         log(f"[bench] decode full {ms_df:.3f} ms = {gbs:.0f} GB/s; window {ms_dw:.4f} ms")
-        decode_obj["kv_cache"] = kv_cache_bench(torch, wl, kvc, args, dinp.lengths, b_full, b_win)
+        decode_obj["kv_cache"] = kv_cache_bench(torch, wl, kvc, args, dinp.lengths, b_full, b_win, flush)
         del kc, vc, kvc
 
     tflops = (flops_full + flops_win) / (ms_step * 1e-3) / 1e12
@@ -704,9 +802,18 @@ def main():
             "window128": {"ms": round(ms_win, 4), "TFLOP/s": round(flops_win / (ms_win * 1e-3) / 1e12, 2),
                           "GB/s": round(bytes_prefill / (ms_win * 1e-3) / 1e9, 1),
                           "frac_hbm_peak": round(bytes_prefill / (ms_win * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "frac_of_copy": round(bytes_prefill / (ms_win * 1e-3) / 1e9 / copy_gbs, 4),
                           "flops": flops_win, "bytes": bytes_prefill},
             "table_ms": round(ms_table, 5),
         },
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+                   "copy_GBps": round(copy_gbs, 1), "copy_frac_hbm_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+                   "copy": "1 GiB device-to-device copy (torch copy_), 2 GiB moved per call, HIP events",
+                   "fill_GBps": round(fill_gbs, 1), "fill": "1 GiB written by torch fill_ (write only)",
+                   "clock_settle_s": args.settle_seconds,
+                   "clock_settle": "each timed section first runs its own calls for clock_settle_s seconds and "
+                                   "then `warmup` rounds, all untimed"},
         "prefill_thd_and_long": other_obj,
         "backward": backward_obj,
         "projection": projection_obj,
@@ -716,7 +823,17 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline, ~{args.cpu_seconds:.0f} s")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        ti0 = wl.tiny()
+        dq0, dk0, dv0 = (inp.q[0].double().numpy(), inp.k[0].double().numpy(), inp.v[0].double().numpy())
+        drows = __import__("numpy").random.default_rng(2024).permutation(S)
+        head = []
+        for w, nm in ((0, "full"), (WINDOW, "window128")):
+            head.append(("tiny_S256", nm, "rows", (ti0.q[0].double().numpy(), ti0.k[0].double().numpy(),
+                                                   ti0.v[0].double().numpy(), ti0.sinks.double().numpy(), w,
+                                                   list(range(256)))))
+            head.append(("dense_B4_S4096_batch0", nm, "rows", (dq0, dk0, dv0, inp.sinks.double().numpy(), w,
+                                                               drows)))
+        result["cpu_baseline"] = cpu_baseline(head + cpu_samples, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -2,10 +2,12 @@
 
 The GPU computes every output; the oracle recomputes seeded samples of them one
 row (query token, all heads) at a time:
-  * dense BSHD prefill B=4, S=4096, full-causal and window-128;
+  * dense BSHD prefill B=4, S=4096, full-causal and window-128: in batch 0 every row on
+    either side of a 32-row boundary (31, 32, 63, 64, ..., 4095) plus 64 seeded rows, in
+    batches 1-3 64 seeded rows each;
   * packed THD prefill, 16 sequences with lengths uniform in [128, 8192];
-  * long-context prefill B=1, S=131072: 512 sampled rows of the window-128 layer, 64 of
-    the full-causal layer (0, 1, 127, 128, 131071 and seeded permutation entries);
+  * long-context prefill B=1, S=131072: the 512 sampled rows (0, 1, 127, 128, 131071 and
+    the first 507 other entries of a seeded permutation), both layers;
   * decode, 64 sequences with cache lengths uniform in [1024, 32768] (all rows).
 Tolerance as in helpers.py.
 """
@@ -54,8 +56,10 @@ def test_dense_bshd(window):
     table = gx.rope_table(4096)
     out = gx.attn_prefill(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), window=window,
                           table=table).cpu()
+    edges = [r for m in range(0, 4096 + 32, 32) for r in (m - 1, m)]   # both sides of every 32-row boundary
     for b in range(4):
-        rows = _rows(4096, 12, 100 + b, must=(0, 31, 32, 63, 64, 127, 128, 4095) if b == 0 else ())
+        rows = _rows(4096, 64, 100 + b, must=edges if b == 0 else ())
+        say(f"  batch {b}: {len(rows)} rows")
         _check_rows(out[b], inp.q[b], inp.k[b], inp.v[b], inp.sinks, window, rows, f"dense b={b} W={window}")
 
 
@@ -75,35 +79,35 @@ def test_thd_16_sequences(window):
                     f"thd seq {n} (L={L}) W={window}")
 
 
-def _long_rows():
-    """Sampled query rows of the 131072-token sequence: 0, 1, 127, 128, 131071 and the
-    first 507 other entries of a seeded permutation (512 rows)."""
-    special = [0, 1, 127, 128, 131071]
-    perm = torch.randperm(131072, generator=torch.Generator().manual_seed(5)).tolist()
-    extra = [r for r in perm if r not in special][:507]
-    return special, extra
-
-
-def test_long_context():
-    say("[gpu] long S=131072")
+@pytest.fixture(scope="module")
+def long_outputs():
+    """Both layers of the 131072-token sequence on the GPU; the sampled rows of their outputs."""
+    say("[gpu] long S=131072: both layers")
     inp = wl.long_context()
     table = gx.rope_table(131072)
     q, k, v, s = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda()
-    special, extra = _long_rows()
-    # window-128 layer: all 512 rows, one oracle call per row (each sees 128 keys)
+    rows = np.array(wl.long_context_rows())
+    outs = {w: gx.attn_prefill(q, k, v, s, window=w, table=table)[0][torch.as_tensor(rows).cuda()].cpu()
+            for w in (0, 128)}
+    del q, k, v, s
+    return inp, rows, outs
+
+
+def test_long_context_window(long_outputs):
+    """Window-128 layer: all 512 sampled rows, one oracle call per row (each sees 128 keys)."""
+    inp, rows, outs = long_outputs
     say("  window=128, 512 rows")
-    out = gx.attn_prefill(q, k, v, s, window=128, table=table)[0].cpu()
-    rows = np.array(sorted(special + extra))
     ref = np.concatenate([oracle.prefill_rows(_Rows(inp.q[0]), _Rows(inp.k[0]), _Rows(inp.v[0]), np64(inp.sinks),
                                               TAU, 128, [r]) for r in rows])
-    assert_close(out[rows], ref, "long W=128 (512 rows)")
-    del out
-    # full-causal layer: the 5 edge rows and the first 59 sampled rows (each sees up to 131072 keys)
-    say("  window=0, 64 rows")
-    out = gx.attn_prefill(q, k, v, s, window=0, table=table)[0].cpu()
-    rows = np.array(sorted(special + extra[:59]))
-    _check_rows(out, inp.q[0], inp.k[0], inp.v[0], inp.sinks, 0, rows, "long W=0 (64 rows)")
-    del out
+    assert_close(outs[128], ref, "long W=128 (512 rows)")
+
+
+def test_long_context_full(long_outputs):
+    """Full-causal layer: all 512 sampled rows in one oracle call (each sees up to 131072 keys)."""
+    inp, rows, outs = long_outputs
+    say("  window=0, 512 rows")
+    ref = oracle.prefill_rows(_Rows(inp.q[0]), _Rows(inp.k[0]), _Rows(inp.v[0]), np64(inp.sinks), TAU, 0, rows)
+    assert_close(outs[0], ref, "long W=0 (512 rows)")
 
 
 def test_over_2g_elements():
