@@ -90,21 +90,16 @@ __device__ __forceinline__ void rope1(float a1, float a2, float cc, float ss, fl
   }
 }
 
-// Rotate 8 pairs: x1 holds dims i..i+7, x2 their partners i+h..i+h+7 (h =
-// rotary_dim / 2), c / s the table's cos / sin for the same i. Writes rounded
-// bf16 outputs.
-__device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const uint4& c,
-                                      const uint4& s, uint4& y1, uint4& y2) {
-  const uint32_t* px1 = reinterpret_cast<const uint32_t*>(&x1);
-  const uint32_t* px2 = reinterpret_cast<const uint32_t*>(&x2);
-  const uint32_t* pc = reinterpret_cast<const uint32_t*>(&c);
-  const uint32_t* ps = reinterpret_cast<const uint32_t*>(&s);
-  uint32_t* py1 = reinterpret_cast<uint32_t*>(&y1);
-  uint32_t* py2 = reinterpret_cast<uint32_t*>(&y2);
-  float r1[8], r2[8];
+// Rotate 2 NW pairs held as NW 32-bit words of two bf16 each: x1 holds dims
+// i..i+2NW-1, x2 their partners i+h.. (h = rotary_dim / 2), c / s the table's
+// cos / sin for the same i. Writes rounded bf16 outputs.
+template <int NW>
+__device__ __forceinline__ void rope_words(const uint32_t* px1, const uint32_t* px2, const uint32_t* pc,
+                                           const uint32_t* ps, uint32_t* py1, uint32_t* py2) {
+  float r1[2 * NW], r2[2 * NW];
   bool fix = false;   // some output may be an inexact result on a bf16 midpoint
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float a1 = h ? bf16_hi(px1[w]) : bf16_lo(px1[w]);
@@ -123,7 +118,7 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
   }
   if (fix) {  // rare: redo every element with the exact fix-up (a no-op where not needed)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         float a1 = h ? bf16_hi(px1[w]) : bf16_lo(px1[w]);
@@ -136,10 +131,25 @@ __device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const ui
     }
   }
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     py1[w] = pack_bf16x2(r1[2 * w], r1[2 * w + 1]);
     py2[w] = pack_bf16x2(r2[2 * w], r2[2 * w + 1]);
   }
+}
+
+// Rotate 8 pairs (16-byte chunks: dims i..i+7 and i+h..i+h+7).
+__device__ __forceinline__ void rope8(const uint4& x1, const uint4& x2, const uint4& c,
+                                      const uint4& s, uint4& y1, uint4& y2) {
+  rope_words<4>(reinterpret_cast<const uint32_t*>(&x1), reinterpret_cast<const uint32_t*>(&x2),
+                reinterpret_cast<const uint32_t*>(&c), reinterpret_cast<const uint32_t*>(&s),
+                reinterpret_cast<uint32_t*>(&y1), reinterpret_cast<uint32_t*>(&y2));
+}
+// Rotate 4 pairs (8-byte chunks).
+__device__ __forceinline__ void rope4(const uint2& x1, const uint2& x2, const uint2& c,
+                                      const uint2& s, uint2& y1, uint2& y2) {
+  rope_words<2>(reinterpret_cast<const uint32_t*>(&x1), reinterpret_cast<const uint32_t*>(&x2),
+                reinterpret_cast<const uint32_t*>(&c), reinterpret_cast<const uint32_t*>(&s),
+                reinterpret_cast<uint32_t*>(&y1), reinterpret_cast<uint32_t*>(&y2));
 }
 
 

@@ -62,6 +62,8 @@ struct PrefillParams {
   int32_t q_shift;
   int32_t kv_len;
   int32_t q_pos0, k_pos0;
+  // window runs (launch_window_runs): query blocks per work group and runs per sequence
+  int32_t run_len, runs_per_seq;
 };
 enum KRotation { KROT_NONE = 0, KROT_FUSED = 1 };
 hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_t stream);
@@ -69,6 +71,12 @@ hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_
 hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t bq, int32_t max_items,
                                int2* work, int32_t* work_count, hipStream_t stream);
 constexpr int kPrefillBQ = 32;   // query positions per work item
+// BSHD window layers of whole sequences, window a multiple of 32 and at most 128:
+// one work group of 8 waves per run of run_len
+// consecutive 32-position query blocks of one (sequence, KV head); k is rotated
+// as it enters the work group's LDS (no separate K pass)
+hipError_t launch_window_runs(const PrefillParams& p, hipStream_t stream);
+constexpr int kWindowRunsTarget = 1024;   // work groups to aim for (four per CU)
 
 // ---- prefill backward ----
 struct BackwardParams {
