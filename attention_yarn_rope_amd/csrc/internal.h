@@ -76,7 +76,7 @@ constexpr int kPrefillBQ = 32;   // query positions per work item
 // consecutive 32-position query blocks of one (sequence, KV head); k is rotated
 // as it enters the work group's LDS (no separate K pass)
 hipError_t launch_window_runs(const PrefillParams& p, hipStream_t stream);
-constexpr int kWindowRunsTarget = 1024;   // work groups to aim for (four per CU)
+constexpr int kWindowRunsTarget = 512;   // work groups to aim for (two per CU, resident together)
 
 // ---- prefill backward ----
 struct BackwardParams {

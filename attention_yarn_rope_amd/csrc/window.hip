@@ -45,6 +45,10 @@ __device__ __forceinline__ float col_xor_sum(float v) {
   return v;
 }
 __device__ __forceinline__ uint4 lds16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void stb16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
 __device__ __forceinline__ void stb8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint2& v) {
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, 0);
@@ -59,7 +63,8 @@ __device__ __forceinline__ uint2 ldb8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return make_uint2(v.x, v.y);
 }
 
-// ROTM: 0 q and k given rotated, 1 all 64 dims rotated, 2 partial rotary (rotary_dim 16, 32 or 48)
+// ROTM: 0 q and k given rotated, 1 all 64 dims rotated, 2 partial rotary (rotary_dim 16, 32 or 48).
+// Two work groups per CU (128 registers a lane, 69 KB of LDS each).
 template <int ROTM>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void window_run_kernel(PrefillParams p) {
@@ -79,8 +84,17 @@ void window_run_kernel(PrefillParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int Hkv = p.num_kv_heads;
-  const int g = blockIdx.x % Hkv;            // consecutive work groups: consecutive KV heads (one per XCD)
-  const int r = blockIdx.x / Hkv;
+  // the KV heads of one run on one XCD (work group i runs on XCD i mod 8), one after another
+  int g, r;
+  const int nwg = gridDim.x;
+  if (nwg % (8 * Hkv) == 0) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    g = k % Hkv;
+    r = (k / Hkv) * 8 + x;
+  } else {
+    g = blockIdx.x % Hkv;
+    r = blockIdx.x / Hkv;
+  }
   const int b = r / p.runs_per_seq;
   const int run = r - b * p.runs_per_seq;
   const int L = p.seqlen;
@@ -155,30 +169,30 @@ void window_run_kernel(PrefillParams p) {
   };
 
   // ---- q of a block: the wave's 32 rows as two 16-column B operands ----
-  uint4 qn[2][2];
+  struct Stage { St st; uint4 q[2][2]; };   // one block's loads in flight: its new key block and q rows
   bf16x8_t qf[2][2];
-  auto load_q = [&](int jq) __attribute__((always_inline)) {
+  auto load_q = [&](int jq, Stage& sg) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int pos = min(jq * SR + 16 * c + col, L - 1);   // rows past the end are never stored
       const bf16_t* qp = qbase + (int64_t)pos * p.q_st + 8 * grp;
-      qn[c][0] = ldg16(qp);
-      qn[c][1] = ldg16(qp + 32);
+      sg.q[c][0] = ldg16(qp);
+      sg.q[c][1] = ldg16(qp + 32);
     }
   };
-  auto rotate_q = [&](int jq) __attribute__((always_inline)) {
+  auto rotate_q = [&](int jq, const Stage& sg) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      uint4 y1 = qn[c][0], y2 = qn[c][1];
+      uint4 y1 = sg.q[c][0], y2 = sg.q[c][1];
       if (ROTM == 1) {
         const bf16_t* tp = tab_s[jq & 1] + (16 * c + col) * TS + 8 * grp;
-        rope8(qn[c][0], qn[c][1], lds16(tp), lds16(tp + 32), y1, y2);
+        rope8(sg.q[c][0], sg.q[c][1], lds16(tp), lds16(tp + 32), y1, y2);
       } else if (ROTM == 2) {   // partial rotary: partners and table rows from global memory
         const int pos = min(jq * SR + 16 * c + col, L - 1);
         const bf16_t* qp = qbase + (int64_t)pos * p.q_st;
         const bf16_t* tp = p.table + (int64_t)min(pos, p.table_rows - 1) * (16 * rc);
-        y1 = rope_chunk_partial(qp, tp, grp, rc, qn[c][0]);
-        y2 = rope_chunk_partial(qp, tp, grp + 4, rc, qn[c][1]);
+        y1 = rope_chunk_partial(qp, tp, grp, rc, sg.q[c][0]);
+        y2 = rope_chunk_partial(qp, tp, grp + 4, rc, sg.q[c][1]);
       }
       qf[c][0] = as_bf16x8(y1);
       qf[c][1] = as_bf16x8(y2);
@@ -193,26 +207,26 @@ void window_run_kernel(PrefillParams p) {
   const bool has_sink = sink > -INFINITY;
 
   // ---- prologue: the run's first block's key blocks, table rows and q ----
+  Stage nx;
   {
     St st[5];
     const int kb0 = max(j0 - WS, 0);
 #pragma unroll
     for (int u = 0; u < 5; ++u)
       if (kb0 + u <= j0) load_block(kb0 + u, kb0 + u == j0, st[u]);
-    load_q(j0);
+    load_q(j0, nx);
 #pragma unroll
     for (int u = 0; u < 5; ++u)
       if (kb0 + u <= j0) store_block(kb0 + u, kb0 + u == j0, st[u]);
   }
   __syncthreads();
-  rotate_q(j0);
+  rotate_q(j0, nx);
 
   for (int j = j0; j < j1; ++j) {
     const bool more = j + 1 < j1;
-    St nx;
     if (more) {   // the next block's new key block and q rows, in flight during this block
-      load_block(j + 1, true, nx);
-      load_q(j + 1);
+      load_block(j + 1, true, nx.st);
+      load_q(j + 1, nx);
     }
 
     // ---- block j: softmax against a reference seeded with the sink logit (a row
@@ -329,7 +343,7 @@ void window_run_kernel(PrefillParams p) {
       // O^T += V^T P^T: V^T from the row-major V rows by transpose reads
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16_t* vb = vt + (4 * grp + (col >> 2)) * RS + 16 * db + 4 * (col & 3);
+        const bf16_t* vb = vt + (4 * grp + (col >> 2)) * RS + 8 * (col & 3) + 4 * (db & 1) + 32 * (db >> 1);
         const uint2 lo = lds_read_tr16(vb);
         const uint2 hi = lds_read_tr16(vb + 16 * RS);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -356,17 +370,19 @@ void window_run_kernel(PrefillParams p) {
       const float lse = (l > 0.0f) ? (ref[c] + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
       stb4(rl, grp == 0 ? (uint32_t)(r * Hq * 4) : 0x7FFFFFF0u, __float_as_uint(lse));
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        uint2 v;
-        v.x = pack_bf16x2(oacc[db][c][0] * inv, oacc[db][c][1] * inv);
-        v.y = pack_bf16x2(oacc[db][c][2] * inv, oacc[db][c][3] * inv);
-        stb8(ro, (uint32_t)(r * orow_b + 2 * (16 * db + 4 * grp)), v);
+      for (int h = 0; h < 2; ++h) {   // dims 32 h + 8 grp .. + 7: accumulators 2 h and 2 h + 1
+        uint4 v;
+        v.x = pack_bf16x2(oacc[2 * h][c][0] * inv, oacc[2 * h][c][1] * inv);
+        v.y = pack_bf16x2(oacc[2 * h][c][2] * inv, oacc[2 * h][c][3] * inv);
+        v.z = pack_bf16x2(oacc[2 * h + 1][c][0] * inv, oacc[2 * h + 1][c][1] * inv);
+        v.w = pack_bf16x2(oacc[2 * h + 1][c][2] * inv, oacc[2 * h + 1][c][3] * inv);
+        stb16(ro, (uint32_t)(r * orow_b + 2 * (32 * h + 8 * grp)), v);
       }
     }
 
-    if (more) store_block(j + 1, true, nx);   // into slot (j + 1) mod 6, which block j does not read
+    if (more) store_block(j + 1, true, nx.st);   // into slot (j + 1) mod 6, which block j does not read
     __syncthreads();
-    if (more) rotate_q(j + 1);
+    if (more) rotate_q(j + 1, nx);
   }
 }
 
