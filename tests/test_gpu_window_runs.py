@@ -1,0 +1,79 @@
+"""GPU parity of the window-run prefill path (BSHD, window a multiple of 32, at most 128).
+
+Such layers run as runs of consecutive 32-query blocks per (sequence, KV head),
+each key rotated once as it enters the run's LDS ring. The cases cover: a
+single position; runs of two blocks and of four (a sequence of 8192 positions
+over 8 KV heads); both work-group placements (the KV heads of a run on one
+XCD when the run count allows it, and the plain one otherwise); ragged tails;
+KV head counts 1, 2, 4 and 8; windows 32, 64, 96 and 128; the natural-log LSE
+output; and equality with the pre-rotated path. The bar is the elementwise
+tolerance in helpers.py against the fp64 oracle on every output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_yarn_rope_amd as gx
+import oracle
+from attention_yarn_rope_amd import workloads as wl
+from helpers import assert_close, np64, say
+
+pytestmark = pytest.mark.gpu
+CFG = oracle.RopeConfig()
+TAU = 0.125
+
+
+@pytest.fixture(scope="module")
+def table():
+    return gx.rope_table(8192)
+
+
+# (B, S, Hkv, window): work groups = B * ceil(ceil(S / 32) / run_len) * Hkv with
+# run_len = max(2, ceil(blocks / 512)); the XCD placement needs a multiple of 8 * Hkv
+CASES = [
+    (1, 1, 1, 128),      # one position, one run of one block
+    (2, 97, 2, 32),      # 4 blocks a sequence, 2 runs: 8 work groups, plain placement
+    (1, 700, 8, 128),    # 22 blocks, 11 runs of 2: 88 work groups, plain placement
+    (3, 513, 1, 64),     # ragged tail of one position
+    (1, 2048, 2, 96),    # 64 blocks, 32 runs: 64 work groups, XCD placement
+    (1, 8192, 8, 128),   # 256 blocks, runs of 4: 512 work groups, XCD placement
+]
+
+
+@pytest.mark.parametrize("B,S,hkv,window", CASES)
+def test_window_runs_against_oracle(table, B, S, hkv, window):
+    inp = wl.prefill_bshd(B, S, seed=800 + S + window, hq=8 * hkv, hkv=hkv)
+    say(f"[gpu] window runs B={B} S={S} Hkv={hkv} W={window}")
+    out = gx.attn_prefill(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), window=window, table=table)
+    ref = oracle.prefill_bshd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.sinks), TAU, window, CFG)
+    assert_close(out, ref, f"B={B} S={S} Hkv={hkv} W={window}")
+
+
+def test_window_runs_lse(table):
+    """The LSE of the window-run path (natural log per row and head) against the oracle's."""
+    B, S, window = 2, 300, 128
+    inp = wl.prefill_bshd(B, S, seed=871)
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    say("[gpu] window runs lse")
+    o, lse = gx.attn_prefill_lse(q, k, v, s, window=window, table=table)
+    dout = np.zeros((B, S, 64, 64))
+    ref = oracle.prefill_bshd_backward(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.sinks), TAU, window, dout, CFG)
+    assert_close(o, ref["o"], "window runs o (lse call)")
+    # the row sum is formed from bf16-rounded probabilities: lse within 2^-8 (+ fp32 log)
+    err = np.abs(np64(lse) - ref["lse"].reshape(B * S, 64))
+    say(f"  lse max_abs={float(err.max()):.3e}")
+    assert float(err.max()) <= 2.0 ** -8 + 1e-4
+
+
+@pytest.mark.parametrize("window", [32, 128])
+def test_window_runs_prerotated_identical(table, window):
+    """Keys rotated as they enter the ring and q rotated in the kernel give the same bits as
+    gptoss_rope_qk followed by the pre-rotated call."""
+    inp = wl.prefill_bshd(2, 450, seed=880 + window)
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    say(f"[gpu] window runs fused == pre-rotated W={window}")
+    a = gx.attn_prefill(q, k, v, s, window=window, table=table)
+    qr, kr = gx.rope_qk(q, k, table)
+    b = gx.attn_prefill(qr, kr, v, s, window=window, table=None)
+    assert torch.equal(a, b)
