@@ -64,6 +64,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {   # the sources a kernel's counters depend on
     "prefill": ["attention_yarn_rope_amd/csrc/prefill.hip", "attention_yarn_rope_amd/csrc/common.h"],
     "decode": ["attention_yarn_rope_amd/csrc/decode.hip", "attention_yarn_rope_amd/csrc/common.h"],
+    "window": ["attention_yarn_rope_amd/csrc/window.hip", "attention_yarn_rope_amd/csrc/common.h"],
 }
 
 
@@ -803,7 +804,8 @@ def main():
                           "GB/s": round(bytes_prefill / (ms_win * 1e-3) / 1e9, 1),
                           "frac_hbm_peak": round(bytes_prefill / (ms_win * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "frac_of_copy": round(bytes_prefill / (ms_win * 1e-3) / 1e9 / copy_gbs, 4),
-                          "flops": flops_win, "bytes": bytes_prefill},
+                          "flops": flops_win, "bytes": bytes_prefill,
+                          "traffic": counters_traffic("prefill_window128_dense_B4_S4096", "window")},
             "table_ms": round(ms_table, 5),
         },
         "device": {"name": torch.cuda.get_device_name(dev),
