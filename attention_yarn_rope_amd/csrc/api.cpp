@@ -306,15 +306,32 @@ gptoss_status prefill_impl(const gptoss_seq_desc* desc, const void* q, const int
     p.k_pos0 = shard->kv_offset;
   }
 
-  if (!thd && !shard && window > 0 && window % bq == 0 && window <= 4 * bq && o_strides[1] >= kHeadDim &&
+  if (!shard && window > 0 && window % bq == 0 && window <= 4 * bq && o_strides[1] >= kHeadDim &&
       o_strides[1] * 2 * bq <= (int64_t)INT32_MAX) {
-    // window layers of whole BSHD sequences: runs of consecutive query blocks, each
-    // key rotated once as it enters the run's LDS ring
-    const int32_t qb = (desc->seqlen + bq - 1) / bq;
-    const int64_t blocks = (int64_t)qb * desc->batch * desc->num_kv_heads;
-    p.run_len = (int32_t)std::max<int64_t>(2, (blocks + kWindowRunsTarget - 1) / kWindowRunsTarget);
-    p.runs_per_seq = (qb + p.run_len - 1) / p.run_len;
-    return hip_status(launch_window_runs(p, s), "window prefill kernel");
+    // window layers of whole sequences: runs of consecutive query blocks, each key
+    // rotated once as it enters the run's LDS ring
+    if (thd) {
+      // runs from the THD schedule with a run of run_len blocks as its unit
+      const int32_t max_blocks = thd_max_items(desc);   // >= sum over sequences of ceil(L / 32)
+      const int64_t blocks = (int64_t)max_blocks * desc->num_kv_heads;
+      p.run_len = (int32_t)std::max<int64_t>(2, (blocks + kWindowRunsTargetThd - 1) / kWindowRunsTargetThd);
+      const int32_t max_runs = (desc->seqlen + bq * p.run_len - 1) / (bq * p.run_len) + desc->batch;
+      int2* work = reinterpret_cast<int2*>(ws);
+      ws += round_up((size_t)max_runs * sizeof(int2));
+      int32_t* count = reinterpret_cast<int32_t*>(ws);
+      st = hip_status(launch_thd_schedule(desc->cu_seqlens, desc->batch, bq * p.run_len, max_runs, work, count, s),
+                      "THD run schedule kernel");
+      if (st != GPTOSS_OK) return st;
+      p.work = work;
+      p.work_count = count;
+      p.q_blocks = max_runs;
+    } else {
+      const int32_t qb = (desc->seqlen + bq - 1) / bq;
+      const int64_t blocks = (int64_t)qb * desc->batch * desc->num_kv_heads;
+      p.run_len = (int32_t)std::max<int64_t>(2, (blocks + kWindowRunsTarget - 1) / kWindowRunsTarget);
+      p.runs_per_seq = (qb + p.run_len - 1) / p.run_len;
+    }
+    return hip_status(launch_window_runs(p, thd, s), "window prefill kernel");
   }
   if (thd) {
     const int32_t max_items = thd_max_items(desc);

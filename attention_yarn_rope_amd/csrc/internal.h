@@ -71,12 +71,15 @@ hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_
 hipError_t launch_thd_schedule(const int32_t* cu_seqlens, int32_t num_seqs, int32_t bq, int32_t max_items,
                                int2* work, int32_t* work_count, hipStream_t stream);
 constexpr int kPrefillBQ = 32;   // query positions per work item
-// BSHD window layers of whole sequences, window a multiple of 32 and at most 128:
-// one work group of 8 waves per run of run_len
-// consecutive 32-position query blocks of one (sequence, KV head); k is rotated
-// as it enters the work group's LDS (no separate K pass)
-hipError_t launch_window_runs(const PrefillParams& p, hipStream_t stream);
-constexpr int kWindowRunsTarget = 512;   // work groups to aim for (two per CU, resident together)
+// Window layers of whole sequences (BSHD or THD), window a multiple of 32 and at
+// most 128: one work group of 8 waves per run of run_len consecutive 32-position
+// query blocks of one (sequence, KV head); k is rotated as it enters the work
+// group's LDS (no separate K pass). BSHD: batch * runs_per_seq runs. THD: the runs
+// come from launch_thd_schedule's list built with bq = 32 * run_len (work,
+// work_count; q_blocks = its capacity).
+hipError_t launch_window_runs(const PrefillParams& p, bool thd, hipStream_t stream);
+constexpr int kWindowRunsTarget = 512;      // BSHD work groups to aim for (two per CU, resident together)
+constexpr int kWindowRunsTargetThd = 1024;  // THD: two rounds, so unequal runs can balance
 
 // ---- prefill backward ----
 struct BackwardParams {

@@ -64,8 +64,9 @@ __device__ __forceinline__ uint2 ldb8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 // ROTM: 0 q and k given rotated, 1 all 64 dims rotated, 2 partial rotary (rotary_dim 16, 32 or 48).
+// THD: packed sequences (runs from the device-built work list) instead of BSHD batches.
 // Two work groups per CU (128 registers a lane, 69 KB of LDS each).
-template <int ROTM>
+template <int ROTM, bool THD>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void window_run_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t ring_k[SLOTS * SR * RS];
@@ -95,20 +96,38 @@ void window_run_kernel(PrefillParams p) {
     g = blockIdx.x % Hkv;
     r = blockIdx.x / Hkv;
   }
-  const int b = r / p.runs_per_seq;
-  const int run = r - b * p.runs_per_seq;
-  const int L = p.seqlen;
-  const int QB = (L + SR - 1) / SR;
-  const int j0 = run * p.run_len;
-  const int j1 = min(j0 + p.run_len, QB);
-  if (b >= p.batch || j0 >= j1) return;
+  // the run: a sequence, its first query block j0 and the block after its last, j1;
+  // tensor offsets of the sequence and the token-major row of its first position
+  int L, j0, j1;
+  int64_t off_q, off_k, off_v, off_o, row0;
+  if (THD) {   // packed sequences: item r of the device-built run list (longest first)
+    if (r >= __ldg(p.work_count)) return;
+    const int2 w = p.work[r];
+    const int n = min(max(w.x, 0), p.batch - 1);
+    const int ts = min(max(__ldg(p.cu_seqlens + n), 0), p.seqlen);
+    const int te = min(max(__ldg(p.cu_seqlens + n + 1), ts), p.seqlen);
+    L = te - ts;
+    j0 = w.y * p.run_len;
+    off_q = (int64_t)ts * p.q_st; off_k = (int64_t)ts * p.k_st; off_v = (int64_t)ts * p.v_st;
+    off_o = (int64_t)ts * p.o_st;
+    row0 = ts;
+  } else {
+    const int b = r / p.runs_per_seq;
+    if (b >= p.batch) return;
+    L = p.seqlen;
+    j0 = (r - b * p.runs_per_seq) * p.run_len;
+    off_q = b * p.q_sb; off_k = b * p.k_sb; off_v = b * p.v_sb; off_o = b * p.o_sb;
+    row0 = (int64_t)b * L;
+  }
+  j1 = min(j0 + p.run_len, (L + SR - 1) / SR);
+  if (j0 < 0 || j0 >= j1) return;
   const int WS = p.window / SR;              // key blocks before the diagonal one (1 .. 4)
   const int head = g * kGroup + wave;
   const float sl = p.scale_log2;
-  const bf16_t* qbase = p.q + b * p.q_sb + (int64_t)head * p.q_sh;
-  const char* kbase = reinterpret_cast<const char*>(p.k + b * p.k_sb + (int64_t)g * p.k_sh);
-  const char* vbase = reinterpret_cast<const char*>(p.v + b * p.v_sb + (int64_t)g * p.v_sh);
-  bf16_t* obase = p.o + b * p.o_sb + (int64_t)head * p.o_sh;
+  const bf16_t* qbase = p.q + off_q + (int64_t)head * p.q_sh;
+  const char* kbase = reinterpret_cast<const char*>(p.k + off_k + (int64_t)g * p.k_sh);
+  const char* vbase = reinterpret_cast<const char*>(p.v + off_v + (int64_t)g * p.v_sh);
+  bf16_t* obase = p.o + off_o + (int64_t)head * p.o_sh;
   const int32_t krow_b = (int32_t)p.k_st * 2, vrow_b = (int32_t)p.v_st * 2;   // < 2^31 / 64 (host check)
   const int32_t orow_b = (int32_t)p.o_st * 2;                                 // < 2^31 / 32 (host check)
   const int Hq = Hkv * kGroup;
@@ -360,7 +379,7 @@ void window_run_kernel(PrefillParams p) {
     const int vrows = min(L - j * SR, SR);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase + (int64_t)j * SR * p.o_st, (vrows - 1) * orow_b + 2 * kHeadDim);
     const __amdgpu_buffer_rsrc_t rl =
-        p.lse ? make_rsrc(p.lse + ((int64_t)b * L + j * SR) * Hq + head, ((vrows - 1) * Hq + 1) * 4)
+        p.lse ? make_rsrc(p.lse + (row0 + j * SR) * Hq + head, ((vrows - 1) * Hq + 1) * 4)
               : make_rsrc(obase, 0);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -386,18 +405,29 @@ void window_run_kernel(PrefillParams p) {
   }
 }
 
+template <bool THD>
+void launch_runs(const PrefillParams& p, uint32_t blocks, hipStream_t stream) {
+  const dim3 grid(blocks), block(NWV * 64);
+  if (!p.table)
+    hipLaunchKernelGGL((window_run_kernel<0, THD>), grid, block, 0, stream, p);
+  else if (p.rot_chunks == kHeadDim / 16)
+    hipLaunchKernelGGL((window_run_kernel<1, THD>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((window_run_kernel<2, THD>), grid, block, 0, stream, p);
+}
+
 }  // namespace
 
-hipError_t launch_window_runs(const PrefillParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.batch * p.runs_per_seq * p.num_kv_heads;
+// BSHD: batch * runs_per_seq runs; THD: q_blocks = the run list's capacity (entries past
+// *work_count exit at once)
+hipError_t launch_window_runs(const PrefillParams& p, bool thd, hipStream_t stream) {
+  const int64_t runs = thd ? (int64_t)p.q_blocks : (int64_t)p.batch * p.runs_per_seq;
+  const int64_t blocks = runs * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  const dim3 grid((uint32_t)blocks), block(NWV * 64);
-  if (!p.table)
-    hipLaunchKernelGGL(window_run_kernel<0>, grid, block, 0, stream, p);
-  else if (p.rot_chunks == kHeadDim / 16)
-    hipLaunchKernelGGL(window_run_kernel<1>, grid, block, 0, stream, p);
+  if (thd)
+    launch_runs<true>(p, (uint32_t)blocks, stream);
   else
-    hipLaunchKernelGGL(window_run_kernel<2>, grid, block, 0, stream, p);
+    launch_runs<false>(p, (uint32_t)blocks, stream);
   return hipGetLastError();
 }
 

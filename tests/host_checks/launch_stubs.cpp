@@ -19,7 +19,7 @@ namespace gptoss {
 hipError_t launch_rope_table(const TableParams&, hipStream_t) { reached("launch_rope_table"); }
 hipError_t launch_rope_qk(const RopeQKParams&, hipStream_t) { reached("launch_rope_qk"); }
 hipError_t launch_prefill(const PrefillParams&, bool, int, hipStream_t) { reached("launch_prefill"); }
-hipError_t launch_window_runs(const PrefillParams&, hipStream_t) { reached("launch_window_runs"); }
+hipError_t launch_window_runs(const PrefillParams&, bool, hipStream_t) { reached("launch_window_runs"); }
 hipError_t launch_thd_schedule(const int32_t*, int32_t, int32_t, int32_t, int2*, int32_t*, hipStream_t) {
   reached("launch_thd_schedule");
 }

@@ -6,7 +6,9 @@ single position; runs of two blocks and of four (a sequence of 8192 positions
 over 8 KV heads); both work-group placements (the KV heads of a run on one
 XCD when the run count allows it, and the plain one otherwise); ragged tails;
 KV head counts 1, 2, 4 and 8; windows 32, 64, 96 and 128; the natural-log LSE
-output; and equality with the pre-rotated path. The bar is the elementwise
+output; equality with the pre-rotated path; and packed THD sequences (runs from
+the device-built run list, lengths from 0 to 4100), also equal bit for bit to
+each sequence run alone as BSHD. The bar is the elementwise
 tolerance in helpers.py against the fp64 oracle on every output.
 """
 
@@ -77,3 +79,49 @@ def test_window_runs_prerotated_identical(table, window):
     qr, kr = gx.rope_qk(q, k, table)
     b = gx.attn_prefill(qr, kr, v, s, window=window, table=None)
     assert torch.equal(a, b)
+
+
+THD_LENGTHS = [0, 1, 31, 32, 33, 700, 1000, 129, 4100, 0, 64]
+
+
+@pytest.mark.parametrize("window", [32, 128])
+def test_window_runs_thd_against_oracle(table, window):
+    """Packed sequences (lengths 0, 1, 31, 32, 33, 64, 129, 700, 1000, 4100): runs from the
+    device-built run list, positions restarting per sequence, against the oracle."""
+    inp = wl.prefill_thd(0, 0, 0, seed=890 + window, lengths=THD_LENGTHS)
+    q, k, v, s, cu = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), inp.cu_seqlens.cuda()
+    say(f"[gpu] window runs THD W={window}")
+    o = gx.attn_prefill(q, k, v, s, window=window, table=table, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    ref = oracle.prefill_thd(np64(inp.q), np64(inp.k), np64(inp.v), inp.cu_seqlens.numpy(), np64(inp.sinks), TAU,
+                             window, CFG)
+    assert_close(o, ref, f"THD W={window}")
+
+
+def test_window_runs_thd_lse(table):
+    """The LSE of packed sequences on the window-run path against the oracle's."""
+    inp = wl.prefill_thd(0, 0, 0, seed=893, lengths=[0, 1, 33, 300, 129])
+    q, k, v, s, cu = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), inp.cu_seqlens.cuda()
+    say("[gpu] window runs THD lse")
+    o, lse = gx.attn_prefill_lse(q, k, v, s, window=128, table=table, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    ref = oracle.prefill_thd_backward(np64(inp.q), np64(inp.k), np64(inp.v), inp.cu_seqlens.numpy(),
+                                      np64(inp.sinks), TAU, 128, np.zeros(tuple(inp.q.shape)), CFG)
+    assert_close(o, ref["o"], "THD o (lse call)")
+    err = np.abs(np64(lse) - ref["lse"])
+    say(f"  lse max_abs={float(err.max()):.3e}")
+    assert float(err.max()) <= 2.0 ** -8 + 1e-4
+
+
+def test_window_runs_thd_equals_per_sequence_bshd(table):
+    """A packed sequence's rows equal the same sequence run alone as BSHD, bit for bit (each
+    block's result does not depend on how the blocks are grouped into runs)."""
+    inp = wl.prefill_thd(0, 0, 0, seed=895, lengths=[700, 33, 1000, 0, 129])
+    q, k, v, s, cu = inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), inp.cu_seqlens.cuda()
+    say("[gpu] window runs THD == per-sequence BSHD")
+    out = gx.attn_prefill(q, k, v, s, window=128, table=table, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    c = inp.cu_seqlens.tolist()
+    for n in range(len(c) - 1):
+        a, b = c[n], c[n + 1]
+        if b == a:
+            continue
+        o = gx.attn_prefill(q[None, a:b], k[None, a:b], v[None, a:b], s, window=128, table=table)
+        assert torch.equal(out[a:b], o[0]), f"sequence {n}"
