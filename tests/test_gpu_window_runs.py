@@ -125,3 +125,21 @@ def test_window_runs_thd_equals_per_sequence_bshd(table):
             continue
         o = gx.attn_prefill(q[None, a:b], k[None, a:b], v[None, a:b], s, window=128, table=table)
         assert torch.equal(out[a:b], o[0]), f"sequence {n}"
+
+
+def test_window_runs_strided_inputs_and_output(table):
+    """q/k/v as views of one fused qkv buffer (token stride 80 heads) and the output written into
+    a strided view: the ring loads and the clipped stores use the given strides."""
+    g = torch.Generator().manual_seed(897)
+    B, S = 2, 333
+    qkv = torch.randn((B, S, 80, 64), generator=g).to(torch.bfloat16)
+    sinks = torch.randn(64, generator=g)
+    d = qkv.cuda()
+    big = torch.zeros((B, S, 96, 64), dtype=torch.bfloat16, device="cuda")
+    out = big[:, :, 16:80]
+    say("[gpu] window runs strided")
+    gx.attn_prefill(d[:, :, :64], d[:, :, 64:72], d[:, :, 72:80], sinks.cuda(), window=128, table=table, out=out)
+    ref = oracle.prefill_bshd(np64(qkv[:, :, :64]), np64(qkv[:, :, 64:72]), np64(qkv[:, :, 72:80]),
+                              np64(sinks), TAU, 128, CFG)
+    assert_close(out, ref, "strided W=128")
+    assert torch.count_nonzero(big[:, :, :16]) == 0 and torch.count_nonzero(big[:, :, 80:]) == 0
