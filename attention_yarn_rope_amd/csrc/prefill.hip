@@ -200,8 +200,14 @@ void prefill_kernel(PrefillParams p) {
     vbase[c] = qkp[c] - lo;
     vlim[c] = (uint32_t)max((int)weff - lo, 0);
   }
-  uint4 qx[CB][2], qt[CB][2];
+  // Every load of the prologue is issued before any result is used, with no
+  // branch between them: a branch between dependent loads makes the wait at its
+  // join cover all loads in flight, which serialises the memory round trips.
+  // The table row depends only on the position, so the lane's two query rows
+  // need two table rows for all CB column blocks.
+  uint4 qx[CB][2], qt[2][2];
   float sink_raw[CB];
+  const bool rot_all = ROTQ && p.rot_chunks == kHeadDim / 16;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int head = g * kGroup + wave * (CB / 2) + (cb >> 1);
@@ -209,17 +215,27 @@ void prefill_kernel(PrefillParams p) {
     const bf16_t* qp = p.q + bb_off_q + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh;
     qx[cb][0] = ldg16(qp + 8 * grp);
     qx[cb][1] = ldg16(qp + 32 + 8 * grp);
-    if (ROTQ && p.rot_chunks == kHeadDim / 16) {
+    sink_raw[cb] = __ldg(p.sinks + head);
+  }
+  if (rot_all) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int pos = min(qpos[c], qlast);
       const bf16_t* tp = p.table + (int64_t)min(pos + p.q_pos0, p.table_rows - 1) * kHeadDim + 8 * grp;
-      qt[cb][0] = ldg16(tp);
-      qt[cb][1] = ldg16(tp + 32);
-    } else if (ROTQ) {
-      // partial rotary: each of the lane's two chunks with its pair partner (prologue only)
+      qt[c][0] = ldg16(tp);
+      qt[c][1] = ldg16(tp + 32);
+    }
+  } else if (ROTQ) {
+    // partial rotary: each of the lane's two chunks with its pair partner (prologue only)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int head = g * kGroup + wave * (CB / 2) + (cb >> 1);
+      const int pos = min(qpos[cb & 1], qlast);
+      const bf16_t* qp = p.q + bb_off_q + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh;
       const bf16_t* tp = p.table + (int64_t)min(pos + p.q_pos0, p.table_rows - 1) * (16 * p.rot_chunks);
       qx[cb][0] = rope_chunk_partial(qp, tp, grp, p.rot_chunks, qx[cb][0]);
       qx[cb][1] = rope_chunk_partial(qp, tp, grp + 4, p.rot_chunks, qx[cb][1]);
     }
-    sink_raw[cb] = __ldg(p.sinks + head);
   }
   float ref[CB], lsum[CB];
   bool unset[CB];        // column without a sink term whose reference is not set yet
@@ -227,7 +243,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     uint4 y1 = qx[cb][0], y2 = qx[cb][1];
-    if (ROTQ && p.rot_chunks == kHeadDim / 16) rope8(qx[cb][0], qx[cb][1], qt[cb][0], qt[cb][1], y1, y2);
+    if (rot_all) rope8(qx[cb][0], qx[cb][1], qt[cb & 1][0], qt[cb & 1][1], y1, y2);
     qf[cb][0] = as_bf16x8(y1);
     qf[cb][1] = as_bf16x8(y2);
     // reference = the sink logit (log2 units); the sink term exp2(sigma - ref) = 1
