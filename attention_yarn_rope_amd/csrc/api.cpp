@@ -489,6 +489,11 @@ gptoss_status gptoss_attn_merge(int32_t num_parts, int32_t tokens, int32_t num_q
 // Backward of the prefill attention.
 // ---------------------------------------------------------------------------
 static int32_t thd_items(const gptoss_seq_desc* d, int bq) { return (d->seqlen + bq - 1) / bq + d->batch; }
+// work items of the backward dq kernel (the length of each head's row of dsigma partials)
+static int64_t bwd_q_items(const gptoss_seq_desc* d) {
+  return d->layout == GPTOSS_THD ? (int64_t)thd_items(d, kPrefillBQ)
+                                 : (int64_t)d->batch * ((d->seqlen + kPrefillBQ - 1) / kPrefillBQ);
+}
 
 size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc) {
   if (check_desc(desc) != GPTOSS_OK) return 0;
@@ -501,6 +506,7 @@ size_t gptoss_attn_prefill_backward_workspace_size(const gptoss_seq_desc* desc) 
   bytes += round_up(T * hq * kHeadDim * sizeof(uint16_t));    // rotated q
   bytes += round_up(T * hkv * kHeadDim * sizeof(uint16_t));   // rotated k
   bytes += round_up(T * hq * 2 * sizeof(float));              // (lse in log2 units, -<dO, o>), head-major
+  bytes += round_up((size_t)bwd_q_items(desc) * hq * sizeof(float));   // dsigma partials, head-major
   return bytes;
 }
 
@@ -543,6 +549,8 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   const int64_t q_row = table ? (int64_t)hq * kHeadDim : q_strides[1];
   if (((int64_t)desc_max_len(desc) + 64) * 2 * std::max(q_row, do_strides[1]) > (int64_t)INT32_MAX)
     return fail(GPTOSS_ERR_UNSUPPORTED, "a sequence's q / dout rows must span less than 2 GiB");
+  if (bwd_q_items(desc) * hkv > (int64_t)INT32_MAX)
+    return fail(GPTOSS_ERR_UNSUPPORTED, "too many 32-query blocks for one launch");
   char* ws = static_cast<char*>(workspace);
 
   BackwardParams p;
@@ -572,6 +580,9 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   uint16_t* krot = reinterpret_cast<uint16_t*>(ws);
   ws += round_up((size_t)T * hkv * kHeadDim * sizeof(uint16_t));
   p.ld = reinterpret_cast<float*>(ws);
+  ws += round_up((size_t)T * hq * 2 * sizeof(float));
+  p.dsink_part = reinterpret_cast<float*>(ws);
+  p.dsink_items = (int32_t)bwd_q_items(desc);
   p.tokens = T;
 
   if (table) {

@@ -22,8 +22,11 @@
 //                      forms D = <dO, o> per row and writes (lse in log2
 //                      units, -D) head-major for the kernels after it; the
 //                      dP sums start from -D, so dP - D needs no subtraction.
-//   bwd_sink_kernel    dsigma per head: one work group per head sums its rows
-//                      in a fixed order (no atomics, reproducible).
+//                      Each work item also sums its rows' share of dsigma per
+//                      head (in a fixed order) into a per-item partial.
+//   bwd_sink_kernel    dsigma per head: one work group per head sums the
+//                      partials of the dq work items in a fixed order (no
+//                      atomics, reproducible).
 //   bwd_kv_kernel      work item (sequence, KV head, 128 keys), 4 waves: wave w
 //                      holds K and V of its own 32 keys as MFMA fragments and
 //                      fp32 dK^T, dV^T for them over all 8 query heads of the
@@ -52,24 +55,19 @@ constexpr int QS = 80;           // LDS row stride of a wave's q / dO tile (dk/d
 
 __device__ __forceinline__ uint2 ldg8(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
-// dsigma_h = - sum over the head's rows of exp(sigma_h - lse) * D, one work
-// group per head, each thread summing a fixed stride of rows, then a tree.
-// lse (log2 units) and -D come head-major from the dq kernel; packed tokens
-// after the last sequence belong to none and are left out.
+// dsigma_h = - sum over the head's rows of exp(sigma_h - lse) * D. The dq
+// kernel leaves one partial per (head, work item): the sum over the item's 32
+// rows. One work group per head adds the partials, each thread a fixed stride
+// of items, then a tree (a fixed order: repeated calls give the same bits).
+// THD items past the schedule's count hold no partial and are left out.
 template <bool THD>
 __global__ __launch_bounds__(256) void bwd_sink_kernel(BackwardParams p) {
   __shared__ float part[256];
   const int h = blockIdx.x;
-  const float sig2 = p.sinks[h] * kLog2e;
-  const float2* ld = reinterpret_cast<const float2*>(p.ld) + (int64_t)h * p.tokens;
-  const int64_t rows = THD ? (int64_t)min(max(__ldg(p.cu_seqlens + p.batch), 0), p.seqlen) : p.tokens;
+  const float* src = p.dsink_part + (int64_t)h * p.dsink_items;
+  const int n = THD ? min(max(__ldg(p.count_q), 0), p.dsink_items) : p.dsink_items;
   float acc = 0.0f;
-  if (sig2 > -INFINITY) {
-    for (int64_t t = threadIdx.x; t < rows; t += 256) {
-      const float2 x = ld[t];
-      acc += __builtin_amdgcn_exp2f(sig2 - x.x) * x.y;   // x.y = -D
-    }
-  }
+  for (int i = threadIdx.x; i < n; i += 256) acc += src[i];
   part[threadIdx.x] = acc;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
@@ -129,7 +127,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     bq_ = b * p.q_sb; bk_ = b * p.k_sb; bv_ = b * p.v_sb; bd_ = b * p.do_sb; bo_ = b * p.o_sb;
   }
   const int q0 = j * BQ;
-  if (j < 0 || q0 >= L) return;
+  if (j < 0 || q0 >= L) {   // an empty item still leaves its (zero) dsigma partial
+    if (lane == 0) p.dsink_part[(int64_t)(g * kGroup + wave) * p.dsink_items + item] = 0.0f;
+    return;
+  }
   const int qlast = min(q0 + BQ, L) - 1;
   const int W = p.window;
   const uint32_t weff = (W > 0) ? (uint32_t)W : 0x7FFFFFFFu;
@@ -168,6 +169,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   bf16x8_t qf[2][2], df[2][2];
   float lse2[2];
   f32x4_t negd[2];   // -D of the lane's query, the starting value of the dP^T sums
+  const float sig2 = __ldg(p.sinks + head) * kLog2e;
+  float dsig = 0.0f;  // this item's share of dsigma for the wave's head: sum of exp2(sig2 - lse2) (-D)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     qpos[cb] = q0 + 16 * cb + col;
@@ -197,8 +200,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     if (grp == 0 && qpos[cb] <= qlast) {
       const int64_t rr = (int64_t)head * p.tokens + row0 + ts + pos;
       reinterpret_cast<float2*>(p.ld)[rr] = make_float2(lse2[cb], -dot);
+      if (sig2 > -INFINITY) dsig += __builtin_amdgcn_exp2f(sig2 - lse2[cb]) * -dot;
     }
   }
+  // the 32 rows' terms sit in lanes 0..15 (2 each); a fixed xor tree over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) dsig += __shfl_xor(dsig, off);
+  if (lane == 0) p.dsink_part[(int64_t)head * p.dsink_items + item] = dsig;
 
   f32x4_t acc[4][2];
 #pragma unroll

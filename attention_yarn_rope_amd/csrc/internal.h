@@ -94,6 +94,8 @@ struct BackwardParams {
   int64_t tokens;                // rows of the token-major tensors (BSHD batch * seqlen, THD seqlen)
   const float* sinks;
   float* dsinks;                 // [Hq]
+  float* dsink_part;             // workspace [Hq, dsink_items]: each dq work item's share of dsigma per head
+  int32_t dsink_items;           // dq work items (BSHD batch * q_blocks, THD max entries of work_q)
   uint16_t* dq; uint16_t* dk; uint16_t* dv;   // contiguous [tokens, H, 64]
   const uint16_t* table;         // NULL: q and k were given already rotated (no rotation back)
   int32_t table_rows;

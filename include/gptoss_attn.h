@@ -242,8 +242,9 @@ gptoss_status gptoss_attn_prefill_lse(const gptoss_seq_desc* desc,
  *   dsinks:  device fp32 [num_q_heads], overwritten (summed over all rows in a
  *            fixed order: repeated calls give identical bits).
  *   workspace: >= gptoss_attn_prefill_backward_workspace_size() bytes, 256-byte
- *            aligned: rotated q and k, per row lse (log2 units) and -D, and
- *            the THD work lists. Its contents are dead after the call.
+ *            aligned: rotated q and k, per row lse (log2 units) and -D, one
+ *            dsigma partial per head and 32-row query block, and the THD work
+ *            lists. Its contents are dead after the call.
  * Errors as for gptoss_attn_prefill; every pointer except table is required.
  * GPTOSS_ERR_UNSUPPORTED if the rows of one sequence of q (or, with a table,
  * of the rotated q) or of dout span 2 GiB or more (the kernels address them

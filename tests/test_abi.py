@@ -279,7 +279,9 @@ def test_backward_argument_errors(lib):
 def test_backward_workspace_size(lib):
     d = _desc_bshd(4, 4096)
     T = 4 * 4096
-    assert lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(d)) == T * 64 * 64 * 2 + T * 8 * 64 * 2 + 2 * T * 64 * 4
+    # rotated q and k, (lse, -D) per row and head, one dsigma partial per head and dq work item (4 x 128)
+    assert lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(d)) == (
+        T * 64 * 64 * 2 + T * 8 * 64 * 2 + 2 * T * 64 * 4 + 4 * 128 * 64 * 4)
     t = SeqDesc(1, 16, 65171, 8179, P, 64, 8, 64)
     ws = lib.gptoss_attn_prefill_backward_workspace_size(ctypes.byref(t))
     assert ws >= 65171 * (64 * 64 * 2 + 8 * 64 * 2 + 2 * 64 * 4) + ((65171 + 31) // 32 + 16) * 8
