@@ -17,7 +17,10 @@
 // wave writes one unnormalised partial (m, l, acc[64]) per query head.
 // Combine kernel: per (sequence, query head) it merges the partials and adds
 // the sink exactly once: M = max(sigma, m_s), l = exp(sigma - M) + sum l_s
-// exp(m_s - M), o = sum acc_s exp(m_s - M) / l (all in log2 units).
+// exp(m_s - M), o = sum acc_s exp(m_s - M) / l (all in log2 units). With one
+// split per sequence (window layers, short caches) the split kernel applies
+// the same formula to its single partial itself, in the same operation order,
+// and no combine kernel runs.
 #include <mutex>
 
 #include "common.h"
@@ -70,7 +73,7 @@ __device__ __forceinline__ KeySpan key_span(const DecodeParams& p, int n) {
 }
 
 template <bool ROTQ, bool PAGED>
-__global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[NW][SUB * DVS];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -234,7 +237,34 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   };
   for (int s0 = c0; s0 < c1; s0 += SUB) step(s0);
   lsum = col_sum(lsum);
-  if (col < kGroup) {
+  if (direct) {
+    // the only split of the sequence: add the sink and normalise here
+    if (col < kGroup) {
+      const int h = g * kGroup + col;
+      const float sig = __ldg(p.sinks + h) * kLog2e;
+      const float M = fmaxf(sig, m);
+      const float Mu = (M == -INFINITY) ? 0.0f : M;
+      const float wgt = __builtin_amdgcn_exp2f(m - Mu);
+      float l = 0.0f;
+      l += lsum * wgt;
+      l += __builtin_amdgcn_exp2f(sig - Mu);
+      bf16_t* op = p.o + (int64_t)n * p.o_sn + (int64_t)h * p.o_sh + 4 * grp;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float o = 0.0f;
+          o += oacc[db][e] * wgt;
+          r[e] = (l > 0.0f) ? o / l : 0.0f;
+        }
+        // out is only 4-byte aligned (even strides): two 32-bit stores
+        uint32_t* o32 = reinterpret_cast<uint32_t*>(op + 16 * db);
+        o32[0] = pack_bf16x2(r[0], r[1]);
+        o32[1] = pack_bf16x2(r[2], r[3]);
+      }
+    }
+  } else if (col < kGroup) {
     const int64_t slot = (((int64_t)n * p.num_kv_heads + g) * p.num_splits + split) * kGroup + col;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -424,7 +454,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((paged ? decode_split_kernel<false, true> : decode_split_kernel<false, false>), grid,
                        dim3(NT), 0, stream, p);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.direct_chunk > 0) return e;   // one split: the split kernel wrote o
   const int waves = p.num_seqs * p.num_kv_heads * kGroup;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((waves + 3) / 4), dim3(NTC), 0, stream, p);
   return hipGetLastError();
