@@ -184,6 +184,34 @@ gptoss_status gptoss_rope_table_init(const gptoss_rope_config* cfg, int32_t num_
   return hip_status(launch_rope_table(p, static_cast<hipStream_t>(stream)), "rope table kernel");
 }
 
+}  // extern "C"
+
+// One tensor (q or k, `heads` heads, layout strides st3) rotated into the
+// contiguous y by the standalone rotation kernel (arguments checked by the caller).
+static gptoss_status rotate_into(const gptoss_seq_desc* desc, const void* x, const int64_t st3[3], void* y,
+                                 int32_t heads, const void* table, int32_t table_rows, int32_t rotary_dim,
+                                 hipStream_t s) {
+  const bool thd = desc->layout == GPTOSS_THD;
+  RopeQKParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.s_b = thd ? 0 : st3[0];
+  p.s_t = st3[1];
+  p.s_h = st3[2];
+  p.y = static_cast<uint16_t*>(y);
+  p.batch = thd ? 1 : desc->batch;
+  p.tokens = desc->seqlen;
+  p.heads = heads;
+  p.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
+  p.num_seqs = desc->batch;
+  p.table = static_cast<const uint16_t*>(table);
+  p.table_rows = table_rows;
+  p.rot_chunks = rotary_dim / 16;
+  p.pos0 = 0;
+  return hip_status(launch_rope_qk(p, s), "rope_qk kernel");
+}
+
+extern "C" {
+
 gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc, const void* q, const int64_t q_strides[3],
                              const void* k, const int64_t k_strides[3], void* q_out, void* k_out,
                              const void* table, int32_t table_rows, int32_t rotary_dim, void* stream) {
@@ -197,30 +225,11 @@ gptoss_status gptoss_rope_qk(const gptoss_seq_desc* desc, const void* q, const i
     return fail(GPTOSS_ERR_UNSUPPORTED, "pointers must be 16-byte aligned and strides multiples of 8 elements");
   st = check_table(table, table_rows, rotary_dim, desc_max_len(desc), true);
   if (st != GPTOSS_OK) return st;
-  const bool thd = desc->layout == GPTOSS_THD;
+  if (desc->layout == GPTOSS_THD && desc->batch == 0) return GPTOSS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int which = 0; which < 2; ++which) {
-    RopeQKParams p;
-    p.x = static_cast<const uint16_t*>(which ? k : q);
-    const int64_t* st3 = which ? k_strides : q_strides;
-    p.s_b = thd ? 0 : st3[0];
-    p.s_t = st3[1];
-    p.s_h = st3[2];
-    p.y = static_cast<uint16_t*>(which ? k_out : q_out);
-    p.batch = thd ? 1 : desc->batch;
-    p.tokens = desc->seqlen;
-    p.heads = which ? desc->num_kv_heads : desc->num_q_heads;
-    p.cu_seqlens = thd ? desc->cu_seqlens : nullptr;
-    p.num_seqs = desc->batch;
-    p.table = static_cast<const uint16_t*>(table);
-    p.table_rows = table_rows;
-    p.rot_chunks = rotary_dim / 16;
-    p.pos0 = 0;
-    if (thd && desc->batch == 0) return GPTOSS_OK;
-    st = hip_status(launch_rope_qk(p, s), "rope_qk kernel");
-    if (st != GPTOSS_OK) return st;
-  }
-  return GPTOSS_OK;
+  st = rotate_into(desc, q, q_strides, q_out, desc->num_q_heads, table, table_rows, rotary_dim, s);
+  if (st != GPTOSS_OK) return st;
+  return rotate_into(desc, k, k_strides, k_out, desc->num_kv_heads, table, table_rows, rotary_dim, s);
 }
 
 }  // extern "C"
@@ -586,9 +595,14 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   p.tokens = T;
 
   if (table) {
-    // rotate q and k once into the workspace (contiguous), exactly as the forward does
-    st = gptoss_rope_qk(desc, q, q_strides, k, k_strides, qrot, krot, table, table_rows, rotary_dim, stream);
+    // k is rotated once into the workspace (contiguous) by the standalone kernel;
+    // the dq kernel rotates q on load, exactly as the forward does, and writes the
+    // rotated rows to the workspace for the dk / dv kernel
+    st = rotate_into(desc, k, k_strides, krot, hkv, table, table_rows, rotary_dim, s);
     if (st != GPTOSS_OK) return st;
+    p.q_in = static_cast<const uint16_t*>(q);
+    p.qi_sb = thd ? 0 : q_strides[0]; p.qi_st = q_strides[1]; p.qi_sh = q_strides[2];
+    p.q_rot = qrot;
     p.q = qrot;
     p.q_sh = kHeadDim; p.q_st = (int64_t)hq * kHeadDim; p.q_sb = thd ? 0 : (int64_t)desc->seqlen * p.q_st;
     p.k = krot;

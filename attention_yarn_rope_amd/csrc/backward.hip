@@ -11,10 +11,13 @@
 // and the rotation is undone with its transpose (the bf16 cast of the rotated
 // q and k passes the gradient through): dq = R^T dq~, dk = R^T dk~.
 //
-// Kernels, in launch order (the caller's q and k are rotated into the
-// workspace first by the standalone rotation kernel):
+// Kernels, in launch order (the caller's k, and with partial rotary also q,
+// is rotated into the workspace first by the standalone rotation kernel):
 //   bwd_dq_kernel      work item (sequence, KV head, 32 query positions): like
-//                      the forward, every K/V tile is staged in LDS once for
+//                      the forward, it rotates its q rows on load (exactly, as
+//                      the standalone rotation does) and also writes them, rotated,
+//                      to the workspace for the dk / dv kernel; every K/V tile
+//                      is staged in LDS once for
 //                      the 8 query heads; per tile a wave runs S^T = K Q^T and
 //                      dP^T = V dO^T (16 + 16 MFMAs), forms dS^T in registers and
 //                      accumulates dQ^T += K^T dS^T (16 MFMAs, K^T read from
@@ -99,7 +102,7 @@ __device__ __forceinline__ uint2 pack4(const f32x4_t& v) {
 // dq: one work group of 8 waves per (sequence, KV head g, 32 query positions);
 // wave w owns query head 8 g + w (two 16-column blocks cb of positions).
 // ---------------------------------------------------------------------------
-template <bool THD, bool ROT>
+template <bool THD, bool ROT, bool ROTIN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_k[2 * NK * KSB];
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * NK * VSB];
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int item = blockIdx.x / Hkv;
   const int g = blockIdx.x - item * Hkv;
   int j, L, ts;
-  int64_t row0, bq_, bk_, bv_, bd_, bo_;
+  int64_t row0, bq_, bk_, bv_, bd_, bo_, bqi_;
   if (THD) {
     if (item >= __ldg(p.count_q)) return;
     const int2 w = p.work_q[item];
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int n = min(max(w.x, 0), p.batch - 1);
     ts = min(max(__ldg(p.cu_seqlens + n), 0), p.seqlen);
     L = min(max(__ldg(p.cu_seqlens + n + 1), ts), p.seqlen) - ts;
-    row0 = 0; bq_ = bk_ = bv_ = bd_ = bo_ = 0;
+    row0 = 0; bq_ = bk_ = bv_ = bd_ = bo_ = bqi_ = 0;
   } else {
     const int r = item / p.batch, b = item - r * p.batch;
     j = p.q_blocks - 1 - r;   // most keys first
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     L = p.seqlen;
     row0 = (int64_t)b * p.seqlen;
     bq_ = b * p.q_sb; bk_ = b * p.k_sb; bv_ = b * p.v_sb; bd_ = b * p.do_sb; bo_ = b * p.o_sb;
+    bqi_ = b * p.qi_sb;
   }
   const int q0 = j * BQ;
   if (j < 0 || q0 >= L) {   // an empty item still leaves its (zero) dsigma partial
@@ -175,12 +179,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   for (int cb = 0; cb < 2; ++cb) {
     qpos[cb] = q0 + 16 * cb + col;
     const int pos = min(qpos[cb], qlast);
-    const bf16_t* qp = p.q + bq_ + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh + 8 * grp;
     const bf16_t* dp = p.dout + bd_ + (int64_t)(ts + pos) * p.do_st + (int64_t)head * p.do_sh + 8 * grp;
     const bf16_t* op = p.o + bo_ + (int64_t)(ts + pos) * p.o_st + (int64_t)head * p.o_sh + 8 * grp;
+    if (ROTIN) {
+      // the caller's q, rotated here with the row's table entries (the two chunks of a
+      // lane are the rotation pairs i, i + 32), then kept for the dk / dv kernel
+      const bf16_t* qp = p.q_in + bqi_ + (int64_t)(ts + pos) * p.qi_st + (int64_t)head * p.qi_sh + 8 * grp;
+      const bf16_t* tp = p.table + (int64_t)min(pos, p.table_rows - 1) * kHeadDim + 8 * grp;
+      const uint4 x1 = ldg16(qp), x2 = ldg16(qp + 32), c = ldg16(tp), sn = ldg16(tp + 32);
+      uint4 y1, y2;
+      rope8(x1, x2, c, sn, y1, y2);
+      qf[cb][0] = as_bf16x8(y1);
+      qf[cb][1] = as_bf16x8(y2);
+      if (qpos[cb] <= qlast) {
+        bf16_t* qr = p.q_rot + ((row0 + ts + pos) * Hq + head) * kHeadDim + 8 * grp;
+        stg16(qr, y1);
+        stg16(qr + 32, y2);
+      }
+    } else {
+      const bf16_t* qp = p.q + bq_ + (int64_t)(ts + pos) * p.q_st + (int64_t)head * p.q_sh + 8 * grp;
+      qf[cb][0] = as_bf16x8(ldg16(qp));
+      qf[cb][1] = as_bf16x8(ldg16(qp + 32));
+    }
     const uint4 d0 = ldg16(dp), d1 = ldg16(dp + 32), o0 = ldg16(op), o1 = ldg16(op + 32);
-    qf[cb][0] = as_bf16x8(ldg16(qp));
-    qf[cb][1] = as_bf16x8(ldg16(qp + 32));
     df[cb][0] = as_bf16x8(d0);
     df[cb][1] = as_bf16x8(d1);
     const float l = p.lse[(row0 + ts + pos) * Hq + head];
@@ -543,8 +564,12 @@ hipError_t launch_all(const BackwardParams& p, hipStream_t stream) {
   const int Hq = p.num_kv_heads * kGroup;
   const int64_t rep = THD ? 1 : p.batch;
   // dq first: it also writes D and lse (log2 units) for the kernels after it
-  hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)), dim3(512), 0,
-                     stream, p);
+  if (ROT && p.q_in)
+    hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, true>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)),
+                       dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, false>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)),
+                       dim3(512), 0, stream, p);
   hipLaunchKernelGGL(bwd_sink_kernel<THD>, dim3(Hq), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT>), dim3((uint32_t)(p.k_tiles * rep * p.num_kv_heads)), dim3(256), 0,
                      stream, p);

@@ -84,6 +84,11 @@ constexpr int kWindowRunsTargetThd = 1024;  // THD: two rounds, so unequal runs 
 // ---- prefill backward ----
 struct BackwardParams {
   const uint16_t* q; int64_t q_sb, q_st, q_sh;     // rotated q (bf16)
+  // Non-NULL: the dq kernel reads the caller's un-rotated q here, rotates it on
+  // load (all 64 dims) and writes the rotated rows to q_rot (= q above,
+  // contiguous) for the dk / dv kernel after it.
+  const uint16_t* q_in; int64_t qi_sb, qi_st, qi_sh;
+  uint16_t* q_rot;
   const uint16_t* k; int64_t k_sb, k_st, k_sh;     // rotated k
   const uint16_t* v; int64_t v_sb, v_st, v_sh;
   const uint16_t* o; int64_t o_sb, o_st, o_sh;     // forward output
