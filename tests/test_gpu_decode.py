@@ -53,6 +53,23 @@ def test_decode_split_counts(table, splits):
     assert (np64(out) - np64(auto)).__abs__().max() <= 2 ** -6
 
 
+def test_decode_single_split_finish_equals_combine(table):
+    """With one split per sequence the split kernel adds the sink and normalises its partial
+    itself (no combine launch). Forcing the planned path (num_splits=2, every sequence shorter
+    than one 128-key split) runs the same single partial through the combine kernel: the two
+    must agree bit for bit, the direct form using the combine's operation order. Lengths 1 to
+    128, sinks including -inf and a large value."""
+    inp = wl.decode(0, 0, 0, seed=26, max_len=128, lengths=[1, 2, 17, 64, 100, 127, 128, 128, 5, 33])
+    inp.sinks[0] = float("-inf")
+    inp.sinks[9] = 30.0
+    say("[gpu] decode one-split finish == combine")
+    for window in (0, 128):
+        direct = _run(inp, window, table)                 # eff <= 512 keys: one split, no combine
+        combined = _run(inp, window, table, num_splits=2)  # 128-key splits: one each, through the combine
+        assert torch.equal(direct, combined), f"window {window}"
+        assert_close(direct, _ref(inp, window), f"decode one split W={window}")
+
+
 def test_decode_equals_last_prefill_row(table):
     """Cache k = rope_qk(k); decode's q is the raw q of the last token."""
     B, S = 2, 777
