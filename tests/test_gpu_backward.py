@@ -133,6 +133,26 @@ def test_backward_prerotated_and_deterministic(table):
     _check((o, lse) + tuple(g1), ref, "pre-rotated")
 
 
+def test_backward_strided_inputs_equal_contiguous(table):
+    """q, k, v as views of one fused qkv buffer (token stride 80 heads), with the table: the dq
+    kernel reads and rotates q through the caller's strides and k is rotated from its own. The
+    gradients equal those of the same values passed contiguous, bit for bit (layout only)."""
+    g = torch.Generator().manual_seed(150)
+    B, S = 2, 333
+    qkv = torch.randn((B, S, 80, 64), generator=g).to(torch.bfloat16).cuda()
+    sinks = torch.randn(64, generator=g).cuda()
+    dout = wl.grad_out((B, S, 64, 64), 1150).cuda()
+    q, k, v = qkv[:, :, :64], qkv[:, :, 64:72], qkv[:, :, 72:80]
+    say("[gpu] backward strided q/k/v == contiguous")
+    for window in (0, 128):
+        o, lse = gx.attn_prefill_lse(q, k, v, sinks, window=window, table=table)
+        strided = gx.attn_prefill_backward(q, k, v, sinks, o, dout, lse, window=window, table=table)
+        contig = gx.attn_prefill_backward(q.contiguous(), k.contiguous(), v.contiguous(), sinks, o, dout, lse,
+                                          window=window, table=table)
+        for name, a, b in zip(("dq", "dk", "dv", "dsinks"), strided, contig):
+            assert torch.equal(a, b), f"{name} window {window}"
+
+
 def test_backward_special_sinks(table):
     """sigma = -inf (no sink: dsigma = 0) and a large sigma = +30 (the sink takes almost all weight)."""
     inp = wl.prefill_bshd(1, 150, seed=140)
