@@ -64,6 +64,7 @@ struct PrefillParams {
   int32_t q_pos0, k_pos0;
   // window runs (launch_window_runs): query blocks per work group and runs per sequence
   int32_t run_len, runs_per_seq;
+  int32_t pair_first;            // BSHD window runs: > 0 splits each two neighbouring runs unevenly (below)
 };
 enum KRotation { KROT_NONE = 0, KROT_FUSED = 1 };
 hipError_t launch_prefill(const PrefillParams& p, bool thd, int krot, hipStream_t stream);

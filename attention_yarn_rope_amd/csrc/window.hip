@@ -111,15 +111,40 @@ void window_run_kernel(PrefillParams p) {
     off_q = (int64_t)ts * p.q_st; off_k = (int64_t)ts * p.k_st; off_v = (int64_t)ts * p.v_st;
     off_o = (int64_t)ts * p.o_st;
     row0 = ts;
+  }
+  int jend;
+  if (THD) {
+    jend = j0 + p.run_len;
+  } else if (p.pair_first > 0) {
+    // Uneven pairs: when every run is resident at once, the first half of the work
+    // groups is dispatched one per CU and the second half fills the other slot; the
+    // older waves win the issue arbitration, so a second-half run advances at about
+    // half the speed of its neighbour until that one ends. Each two neighbouring
+    // runs of a sequence therefore cover 2 run_len blocks as pair_first blocks for
+    // the first-half run and the rest for the second-half run, so both end at about
+    // the same time.
+    const int half = p.batch * p.runs_per_seq / 2;
+    const bool second = r >= half;
+    const int pr = second ? r - half : r;
+    const int pps = p.runs_per_seq / 2;   // pairs per sequence
+    const int b = pr / pps;
+    if (b >= p.batch) return;
+    L = p.seqlen;
+    const int base = (pr - b * pps) * 2 * p.run_len;
+    j0 = second ? base + p.pair_first : base;
+    jend = second ? base + 2 * p.run_len : base + p.pair_first;
+    off_q = b * p.q_sb; off_k = b * p.k_sb; off_v = b * p.v_sb; off_o = b * p.o_sb;
+    row0 = (int64_t)b * L;
   } else {
     const int b = r / p.runs_per_seq;
     if (b >= p.batch) return;
     L = p.seqlen;
     j0 = (r - b * p.runs_per_seq) * p.run_len;
+    jend = j0 + p.run_len;
     off_q = b * p.q_sb; off_k = b * p.k_sb; off_v = b * p.v_sb; off_o = b * p.o_sb;
     row0 = (int64_t)b * L;
   }
-  j1 = min(j0 + p.run_len, (L + SR - 1) / SR);
+  j1 = min(jend, (L + SR - 1) / SR);
   if (j0 < 0 || j0 >= j1) return;
   const int WS = p.window / SR;              // key blocks before the diagonal one (1 .. 4)
   const int head = g * kGroup + wave;
