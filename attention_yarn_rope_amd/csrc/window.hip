@@ -1,5 +1,5 @@
-// Sliding-window prefill as runs of consecutive query blocks (BSHD; window a
-// multiple of 32, at most 128: GPT-OSS's 128-token layers).
+// Sliding-window prefill as runs of consecutive query blocks (BSHD or packed
+// THD; window a multiple of 32, at most 128: GPT-OSS's 128-token layers).
 //
 // What is computed is the prefill attention of prefill.hip (page
 // "nemo_automodel.components.models.gpt_oss.layers", GptOssAttention: sinks,
@@ -20,6 +20,11 @@
 // staged in LDS. One barrier per block. Each block computes W/32 + 1 steps of 32
 // keys: the first with key k of the step visible to query row i iff k > i, the
 // last (the diagonal block) iff k <= i, the ones between fully visible.
+//
+// Runs: BSHD sequences are cut into runs of run_len blocks, all resident at
+// once (two work groups per CU), two neighbouring runs split unevenly (see the
+// work-item mapping) so that the two work groups of a CU end together; THD runs
+// come from a device-built list, longest first, in about two rounds.
 #include "common.h"
 #include "internal.h"
 
