@@ -596,6 +596,8 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   } else {
     p.q_blocks = (desc->seqlen + kPrefillBQ - 1) / kPrefillBQ;
     p.k_tiles = (desc->seqlen + kBackwardKT - 1) / kBackwardKT;
+    // full causal, a multiple of 4 key tiles: two tiles per dk / dv work group, balanced
+    p.kv_pairs = (window == 0 && p.k_tiles % 4 == 0) ? 1 : 0;
   }
   uint16_t* qrot = reinterpret_cast<uint16_t*>(ws);
   ws += round_up((size_t)T * hq * kHeadDim * sizeof(uint16_t));

@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int Hkv = p.num_kv_heads;
   const int item = blockIdx.x / Hkv;
   const int g = blockIdx.x - item * Hkv;
-  int jt, L, ts;
+  int jt0, jt1 = -1, L, ts;
   int64_t row0, bq_, bk_, bv_, bd_;
   if (THD) {
     if (item >= __ldg(p.count_k)) return;
@@ -359,18 +359,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int n = min(max(w.x, 0), p.batch - 1);
     ts = min(max(__ldg(p.cu_seqlens + n), 0), p.seqlen);
     L = min(max(__ldg(p.cu_seqlens + n + 1), ts), p.seqlen) - ts;
-    jt = (L + KT - 1) / KT - 1 - w.y;   // the list counts tiles from the end: most queries first
+    jt0 = (L + KT - 1) / KT - 1 - w.y;   // the list counts tiles from the end: most queries first
     row0 = 0; bq_ = bk_ = bv_ = bd_ = 0;
   } else {
-    const int r = item / p.batch, b = item - r * p.batch;
-    jt = r;                   // tile 0 is seen by every query: most work first
+    int r, b;
+    if (p.kv_pairs) {
+      // Full causal: key tile t is seen by the queries from 128 t on, so its work falls
+      // linearly with t. Each work group takes two tiles. The first half of the grid
+      // (dispatched first, one per CU, and faster: the older waves win the issue
+      // arbitration) takes {i, 3T/4 - 1 - i}, the second half {T/4 + i, T - 1 - i},
+      // i < T/4: 5T/4 + 1 against 3T/4 + 1 tiles of work, so that both end together.
+      const int T = p.k_tiles, q4 = T / 4, half = p.batch * q4;
+      const bool second = item >= half;
+      const int it2 = second ? item - half : item;
+      r = it2 / p.batch;
+      b = it2 - r * p.batch;
+      jt0 = second ? q4 + r : r;
+      jt1 = second ? T - 1 - r : 3 * q4 - 1 - r;
+    } else {
+      r = item / p.batch;
+      b = item - r * p.batch;
+      jt0 = r;                  // tile 0 is seen by every query: most work first
+    }
     ts = 0;
     L = p.seqlen;
     row0 = (int64_t)b * p.seqlen;
     bq_ = b * p.q_sb; bk_ = b * p.k_sb; bv_ = b * p.v_sb; bd_ = b * p.do_sb;
   }
+  for (int pi = 0; pi < 2; ++pi) {
+  const int jt = pi ? jt1 : jt0;
   const int t0 = jt * KT;
-  if (jt < 0 || t0 >= L) return;   // uniform over the work group
+  if (jt < 0 || t0 >= L) continue;   // uniform over the work group
   const int tlast = min(t0 + KT, L) - 1;
   const int k0 = t0 + 32 * wave;   // the wave's first key (past tlast: the wave only helps fetch)
   const int W = p.window;
@@ -552,6 +571,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       *reinterpret_cast<uint2*>(p.dv + orow + 16 * pr + 32) = pack4(dvt[pr + 2][kb]);
     }
   }
+  }   // key tiles of the work group
 }
 
 __global__ __launch_bounds__(256) void fill_f32_kernel(float* x, int32_t n, float value) {
@@ -571,8 +591,9 @@ hipError_t launch_all(const BackwardParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, false>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)),
                        dim3(512), 0, stream, p);
   hipLaunchKernelGGL(bwd_sink_kernel<THD>, dim3(Hq), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT>), dim3((uint32_t)(p.k_tiles * rep * p.num_kv_heads)), dim3(256), 0,
-                     stream, p);
+  const int64_t kv_items = p.kv_pairs ? (int64_t)p.k_tiles / 2 * rep : (int64_t)p.k_tiles * rep;
+  hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT>), dim3((uint32_t)(kv_items * p.num_kv_heads)), dim3(256), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

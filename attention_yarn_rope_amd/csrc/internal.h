@@ -113,7 +113,8 @@ struct BackwardParams {
   float scale_log2;              // softmax_scale * log2(e)
   const int32_t* cu_seqlens;     // THD
   int32_t q_blocks;              // BSHD: ceil(S / 32); THD: max entries of work_q
-  int32_t k_tiles;               // BSHD: ceil(S / 64); THD: max entries of work_k
+  int32_t k_tiles;               // BSHD: ceil(S / 128) key tiles; THD: max entries of work_k
+  int32_t kv_pairs;              // BSHD full causal: each dk / dv work group takes two key tiles (below)
   const int2* work_q; const int32_t* count_q;   // THD: (sequence, query block), most keys first
   const int2* work_k; const int32_t* count_k;   // THD: (sequence, key tile counted from the end), most queries first
 };

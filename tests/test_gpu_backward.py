@@ -80,6 +80,16 @@ def test_backward_bshd(table, B, S, window):
     _check(got, ref, f"B={B} S={S} W={window}")
 
 
+@pytest.mark.parametrize("B,S", [(2, 512), (1, 1024)])
+def test_backward_full_causal_tile_pairs(table, B, S):
+    """Full-causal layers with a multiple of 4 key tiles of 128 give each dk / dv work group two
+    tiles of complementary work ({i, 3T/4 - 1 - i} and {T/4 + i, T - 1 - i}); every key of every
+    tile against the oracle (T = 4 and 8)."""
+    say(f"[gpu] backward tile pairs B={B} S={S}")
+    got, ref = _bshd_case(B, S, 0, table, seed=70 + S)
+    _check(got, ref, f"tile pairs B={B} S={S}")
+
+
 @pytest.mark.parametrize("window", [0, 300])
 def test_backward_ragged_long(table, window):
     say(f"[gpu] backward bshd B=2 S=700 W={window}")
