@@ -53,7 +53,7 @@ namespace {
 constexpr int BQ = kPrefillBQ;   // query positions per block
 constexpr int NK = kBackwardNK;  // keys per tile
 constexpr int KSB = 80;          // LDS row stride of the K tile (dq kernel): conflict-free transpose reads
-constexpr int VSB = 72;          // LDS row stride of the V tile (dq kernel): conflict-free 16 B row reads
+constexpr int VSB = 80;          // LDS row stride of the V tile (dq kernel): 16 B row reads (72 measured 0.5 % slower)
 constexpr int QS = 80;           // LDS row stride of a wave's q / dO tile (dk/dv kernel)
 
 __device__ __forceinline__ uint2 ldg8(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
