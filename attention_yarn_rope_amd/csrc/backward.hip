@@ -41,8 +41,8 @@
 //                      dK^T += Q^T dS (8 + 8 MFMAs, dO^T and Q^T by transpose
 //                      reads). Each step's 32 q and dO rows and their (lse, -D)
 //                      words are fetched by the 4 waves together, a quarter each,
-//                      during the step before, into the other half of a
-//                      double-buffered LDS tile: one barrier per step.
+//                      two steps ahead, into a ring of four LDS tiles: one barrier
+//                      per two steps.
 // dq, dk, dv are written once each (no atomics), rounded to bf16 from fp32.
 #include "common.h"
 #include "internal.h"
@@ -335,17 +335,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 // Wave w holds K and V of the 32 keys t0 + 32 w .. + 31 as MFMA fragments and
 // fp32 dK^T, dV^T for them (64 VGPRs) over all 8 query heads of the group, so no
 // sum across waves is needed. The 4 waves walk the same steps (32 queries of
-// one head each) and share each step's q / dO rows through a double-buffered
-// LDS tile that each wave fills a quarter of: a row is fetched once per work
-// group, not once per wave.
+// one head each) and share each step's q / dO rows through LDS tiles that each
+// wave fills a quarter of: a row is fetched once per work group, not once per
+// wave.
 // ---------------------------------------------------------------------------
 constexpr int KT = kBackwardKT;   // keys per work group
 static_assert(KT == 4 * 32, "one wave per 32 keys");
 
 template <bool THD, bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds_t[2][2 * BQ * QS];   // [buffer][q tile, dO tile]
-  __shared__ __attribute__((aligned(16))) float lds_ld[2][2 * BQ];        // [buffer][lse of 32 queries, -D of 32]
+  __shared__ __attribute__((aligned(16))) bf16_t lds_t[4][2 * BQ * QS];   // [buffer][q tile, dO tile]
+  __shared__ __attribute__((aligned(16))) float lds_ld[4][2 * BQ];        // [buffer][lse of 32 queries, -D of 32]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int Hkv = p.num_kv_heads;
@@ -423,9 +423,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // queries come with them, one per lane.
   const int srow = 8 * wave + (lane >> 3), sch = lane & 7;
   const int32_t qrow_b = (int32_t)p.q_st * 2, drow_b = (int32_t)p.do_st * 2;
-  uint4 sq, sd;
-  uint32_t sw;
-  auto fetch = [&](int qb, int hh) __attribute__((always_inline)) {
+  struct Fetch { uint4 q, d; uint32_t w; };
+  auto fetch = [&](int qb, int hh, Fetch& f) __attribute__((always_inline)) {
     const int q0 = qb * BQ;
     const int head = g * kGroup + hh;
     const __amdgpu_buffer_rsrc_t rq =
@@ -433,16 +432,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const __amdgpu_buffer_rsrc_t rd =
         make_rsrc(p.dout + bd_ + (int64_t)ts * p.do_st + (int64_t)head * p.do_sh, (L - 1) * drow_b + 2 * kHeadDim);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.ld + 2 * ((int64_t)head * p.tokens + row0 + ts), L * 8);
-    sq = ldb16(rq, (uint32_t)((q0 + srow) * qrow_b + 16 * sch));
-    sd = ldb16(rd, (uint32_t)((q0 + srow) * drow_b + 16 * sch));
-    sw = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)((2 * q0 + lane) * 4), 0, 0);
+    f.q = ldb16(rq, (uint32_t)((q0 + srow) * qrow_b + 16 * sch));
+    f.d = ldb16(rd, (uint32_t)((q0 + srow) * drow_b + 16 * sch));
+    f.w = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)((2 * q0 + lane) * 4), 0, 0);
   };
-  auto write_tile = [&](int buf) __attribute__((always_inline)) {
+  auto write_tile = [&](int buf, const Fetch& f) __attribute__((always_inline)) {
     bf16_t* lq = lds_t[buf];
-    *reinterpret_cast<uint4*>(lq + srow * QS + 8 * sch) = sq;
-    *reinterpret_cast<uint4*>(lq + BQ * QS + srow * QS + 8 * sch) = sd;
+    *reinterpret_cast<uint4*>(lq + srow * QS + 8 * sch) = f.q;
+    *reinterpret_cast<uint4*>(lq + BQ * QS + srow * QS + 8 * sch) = f.d;
     // words 16 w .. 16 w + 15 of the 64, split into the lse and -D vectors
-    if ((lane >> 4) == wave) lds_ld[buf][(lane & 1) * BQ + (lane >> 1)] = __uint_as_float(sw);
+    if ((lane >> 4) == wave) lds_ld[buf][(lane & 1) * BQ + (lane >> 1)] = __uint_as_float(f.w);
   };
 
   // One step: 32 queries (block qb) of head hh against the wave's 32 keys, from
@@ -534,20 +533,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // one down, each for the 8 query heads. The work groups of one (sequence, KV
   // head) run together on one XCD (consecutive work groups take consecutive KV
   // heads, dealt round-robin over the 8 XCDs) and then read the same q / dO
-  // block at about the same time, so L2 serves the repeats. A step's rows are
-  // fetched during the step before and written to the other LDS buffer at its
-  // end; one barrier per step. The last step fetches its own rows again (no
-  // branch around the loads).
+  // block at about the same time, so L2 serves the repeats. Two steps per
+  // barrier (nsteps is a multiple of kGroup, so even): the rows of steps s + 2
+  // and s + 3 load while s and s + 1 compute and are written to the other two of
+  // four LDS buffers at the end (with one step per barrier the layer took 1 %
+  // longer). The last two steps fetch the last step's rows again (no branch
+  // around the loads).
   const int qb_lo = t0 / BQ, qb_hi = qhi / BQ;
   const int nsteps = (qb_hi - qb_lo + 1) * kGroup;
-  fetch(qb_hi, 0);
-  write_tile(0);
+  Fetch fa, fb;
+  fetch(qb_hi, 0, fa);
+  fetch(qb_hi, 1, fb);
+  write_tile(0, fa);
+  write_tile(1, fb);
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int n = min(s + 1, nsteps - 1);
-    fetch(qb_hi - n / kGroup, n % kGroup);
-    step(s & 1, qb_hi - s / kGroup);
-    write_tile((s & 1) ^ 1);
+  for (int s = 0; s < nsteps; s += 2) {
+    const int na = min(s + 2, nsteps - 1), nb = min(s + 3, nsteps - 1);
+    fetch(qb_hi - na / kGroup, na % kGroup, fa);
+    fetch(qb_hi - nb / kGroup, nb % kGroup, fb);
+    step(s & 3, qb_hi - s / kGroup);
+    step((s + 1) & 3, qb_hi - (s + 1) / kGroup);
+    write_tile((s + 2) & 3, fa);
+    write_tile((s + 3) & 3, fb);
     __syncthreads();
   }
 
