@@ -571,7 +571,7 @@ gptoss_status gptoss_attn_prefill_backward(const gptoss_seq_desc* desc, const vo
   const int64_t q_row = table ? (int64_t)hq * kHeadDim : q_strides[1];
   if (((int64_t)desc_max_len(desc) + 64) * 2 * std::max(q_row, do_strides[1]) > (int64_t)INT32_MAX)
     return fail(GPTOSS_ERR_UNSUPPORTED, "a sequence's q / dout rows must span less than 2 GiB");
-  if (bwd_q_items(desc) * hkv > (int64_t)INT32_MAX)
+  if (bwd_q_items(desc) * hkv * 2 > (int64_t)INT32_MAX)
     return fail(GPTOSS_ERR_UNSUPPORTED, "too many 32-query blocks for one launch");
   char* ws = static_cast<char*>(workspace);
 

@@ -17,8 +17,9 @@
 //                      the forward, it rotates its q rows on load (exactly, as
 //                      the standalone rotation does) and also writes them, rotated,
 //                      to the workspace for the dk / dv kernel; every K/V tile
-//                      is staged in LDS once for
-//                      the 8 query heads; per tile a wave runs S^T = K Q^T and
+//                      is staged in LDS once for the 8 query heads (full layers:
+//                      one 8-wave work group; window layers: two 4-wave groups,
+//                      4 heads each, two per CU); per tile a wave runs S^T = K Q^T and
 //                      dP^T = V dO^T (16 + 16 MFMAs), forms dS^T in registers and
 //                      accumulates dQ^T += K^T dS^T (16 MFMAs, K^T read from
 //                      the row-major K tile with ds_read_b64_tr_b16). It also
@@ -99,18 +100,28 @@ __device__ __forceinline__ uint2 pack4(const f32x4_t& v) {
 }
 
 // ---------------------------------------------------------------------------
-// dq: one work group of 8 waves per (sequence, KV head g, 32 query positions);
-// wave w owns query head 8 g + w (two 16-column blocks cb of positions).
+// dq: WAVES waves per (sequence, KV head g, 32 query positions) and work group:
+// 8 (one work group per CU, each K/V tile staged once for the whole group) or 4
+// (two work groups per (sequence, g, block), 8 / WAVES = 2 head halves, two per
+// CU, so that one group's prologue overlaps the other's tiles: short items).
+// Wave w owns query head 8 g + WAVES * half + w (two 16-column blocks cb of
+// positions).
 // ---------------------------------------------------------------------------
-template <bool THD, bool ROT, bool ROTIN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BackwardParams p) {
+template <bool THD, bool ROT, bool ROTIN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds_k[2 * NK * KSB];
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * NK * VSB];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
+  constexpr int NTH = 64 * WAVES;
+  constexpr int HALVES = kGroup / WAVES;
   const int Hkv = p.num_kv_heads, Hq = Hkv * kGroup;
-  const int item = blockIdx.x / Hkv;
-  const int g = blockIdx.x - item * Hkv;
+  // consecutive work groups take consecutive KV heads (one XCD per KV head with 8 of
+  // them), then the head halves, then the items
+  const int g = blockIdx.x % Hkv;
+  const int hv = (int)(blockIdx.x / Hkv);
+  const int item = hv / HALVES;
+  const int half = hv - item * HALVES;
   int j, L, ts;
   int64_t row0, bq_, bk_, bv_, bd_, bo_, bqi_;
   if (THD) {
@@ -132,7 +143,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   }
   const int q0 = j * BQ;
   if (j < 0 || q0 >= L) {   // an empty item still leaves its (zero) dsigma partial
-    if (lane == 0) p.dsink_part[(int64_t)(g * kGroup + wave) * p.dsink_items + item] = 0.0f;
+    if (lane == 0) p.dsink_part[(int64_t)(g * kGroup + WAVES * half + wave) * p.dsink_items + item] = 0.0f;
     return;
   }
   const int qlast = min(q0 + BQ, L) - 1;
@@ -142,24 +153,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int kv_hi = qlast + 1;
   const int ntiles = (kv_hi - kv_lo + NK - 1) / NK;
   const float sl = p.scale_log2;
-  const int head = g * kGroup + wave;
+  const int head = g * kGroup + WAVES * half + wave;
 
-  // staging: thread -> (row tid / 8, 16-byte chunk tid % 8) of the K and V tiles
+  // staging: thread -> (rows tid / 8 + NTH / 8 i, 16-byte chunk tid % 8) of the K and V tiles
+  constexpr int SP = 64 * 8 / NTH;   // rows per thread
   const int srow = tid >> 3, scc = tid & 7;
   const int32_t krow_b = (int32_t)p.k_st * 2, vrow_b = (int32_t)p.v_st * 2;
   const char* k_tile0 = reinterpret_cast<const char*>(p.k + bk_ + (int64_t)(ts + kv_lo) * p.k_st + (int64_t)g * p.k_sh);
   const char* v_tile0 = reinterpret_cast<const char*>(p.v + bv_ + (int64_t)(ts + kv_lo) * p.v_st + (int64_t)g * p.v_sh);
   const uint32_t koff = (uint32_t)(srow * krow_b + 16 * scc);
   const uint32_t voff = (uint32_t)(srow * vrow_b + 16 * scc);
-  uint4 sk, sv;
+  uint4 sk[SP], sv[SP];
   auto load_tile = [&](int t) __attribute__((always_inline)) {
     const int rows = min(kv_hi - (kv_lo + t * NK), NK);   // the tile's own rows: the range stays < 2^31 bytes
-    sk = ldb16(make_rsrc(k_tile0 + (int64_t)t * NK * krow_b, (rows - 1) * krow_b + 2 * kHeadDim), koff);
-    sv = ldb16(make_rsrc(v_tile0 + (int64_t)t * NK * vrow_b, (rows - 1) * vrow_b + 2 * kHeadDim), voff);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_tile0 + (int64_t)t * NK * krow_b, (rows - 1) * krow_b + 2 * kHeadDim);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_tile0 + (int64_t)t * NK * vrow_b, (rows - 1) * vrow_b + 2 * kHeadDim);
+#pragma unroll
+    for (int i = 0; i < SP; ++i) {
+      sk[i] = ldb16(rk, koff + (uint32_t)(i * (NTH / 8) * krow_b));
+      sv[i] = ldb16(rv, voff + (uint32_t)(i * (NTH / 8) * vrow_b));
+    }
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(lds_k + buf * NK * KSB + srow * KSB + 8 * scc) = sk;
-    *reinterpret_cast<uint4*>(lds_v + buf * NK * VSB + srow * VSB + 8 * scc) = sv;
+#pragma unroll
+    for (int i = 0; i < SP; ++i) {
+      *reinterpret_cast<uint4*>(lds_k + buf * NK * KSB + (srow + i * (NTH / 8)) * KSB + 8 * scc) = sk[i];
+      *reinterpret_cast<uint4*>(lds_v + buf * NK * VSB + (srow + i * (NTH / 8)) * VSB + 8 * scc) = sv[i];
+    }
   };
 
   if (ntiles > 0) load_tile(0);
@@ -591,12 +611,19 @@ hipError_t launch_all(const BackwardParams& p, hipStream_t stream) {
   const int Hq = p.num_kv_heads * kGroup;
   const int64_t rep = THD ? 1 : p.batch;
   // dq first: it also writes D and lse (log2 units) for the kernels after it
-  if (ROT && p.q_in)
-    hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, true>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)),
-                       dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, false>), dim3((uint32_t)(p.q_blocks * rep * p.num_kv_heads)),
-                       dim3(512), 0, stream, p);
+  // window layers (a few key tiles per item): 4-wave work groups, two per CU
+  const uint32_t nq = (uint32_t)(p.q_blocks * rep * p.num_kv_heads);
+  if (p.window > 0) {
+    if (ROT && p.q_in)
+      hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, true, 4>), dim3(2 * nq), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, false, 4>), dim3(2 * nq), dim3(256), 0, stream, p);
+  } else {
+    if (ROT && p.q_in)
+      hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, true, 8>), dim3(nq), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<THD, ROT, false, 8>), dim3(nq), dim3(512), 0, stream, p);
+  }
   hipLaunchKernelGGL(bwd_sink_kernel<THD>, dim3(Hq), dim3(256), 0, stream, p);
   const int64_t kv_items = p.kv_pairs ? (int64_t)p.k_tiles / 2 * rep : (int64_t)p.k_tiles * rep;
   hipLaunchKernelGGL((bwd_kv_kernel<THD, ROT>), dim3((uint32_t)(kv_items * p.num_kv_heads)), dim3(256), 0, stream,
