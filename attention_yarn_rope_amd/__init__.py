@@ -28,6 +28,8 @@ from .api import (  # noqa: F401
     decode_kv_workspace_size,
     prefill_workspace_size,
     prefill_backward_workspace_size,
+    check_lengths,
+    LENGTH_FAULTS,
     decode_workspace_size,
 )
 from ._lib import GptossError, load as load_library  # noqa: F401

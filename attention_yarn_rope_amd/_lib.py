@@ -40,6 +40,7 @@ CACHE_KINDS = {"contiguous": 0, "paged": 1, "ring": 2}
 # name -> (restype, argtypes); every symbol include/gptoss_attn.h declares
 SIGNATURES = {
     "gptoss_abi_version": (ctypes.c_int, []),
+    "gptoss_check_lengths": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "gptoss_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gptoss_last_error": (ctypes.c_char_p, []),
     "gptoss_yarn_params": (ctypes.c_int, [ctypes.POINTER(RopeConfig), ctypes.POINTER(c_f64),

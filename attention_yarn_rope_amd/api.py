@@ -448,3 +448,24 @@ def attn_merge(o_parts, lse_parts, sinks=None, out=None, lse_out=None):
         P, T, Hq, D, _ptr(o_parts), (ctypes.c_int64 * 4)(ps[0], ps[1], ps[2], ps[3]), _ptr(lse_parts),
         _ptr(sinks), _ptr(out), I64x2(out.stride(0), out.stride(1)), _ptr(lse_out), _stream()))
     return out
+
+
+LENGTH_FAULTS = {"cu_start": 1, "cu_order": 2, "cu_total": 4, "cache": 8}
+
+
+def check_lengths(cu_seqlens=None, total_tokens=-1, cache_seqlens=None, max_cache_len=1, result=None):
+    """Check device-resident lengths on the device (no synchronisation): returns an int32 [3]
+    device tensor: OR of the LENGTH_FAULTS bits of the broken rules (0: all hold), the first
+    offending cu_seqlens index and the first offending cache_seqlens index (-1: none)."""
+    for name, t in (("cu_seqlens", cu_seqlens), ("cache_seqlens", cache_seqlens)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 tensor on the device")
+    dev = (cu_seqlens if cu_seqlens is not None else cache_seqlens)
+    if result is None:
+        result = torch.empty(3, dtype=torch.int32, device=dev.device if dev is not None else "cuda")
+    batch = cu_seqlens.numel() - 1 if cu_seqlens is not None else 0
+    n = cache_seqlens.numel() if cache_seqlens is not None else 0
+    check("gptoss_check_lengths", _lib.load().gptoss_check_lengths(
+        _ptr(cu_seqlens), batch, int(total_tokens), _ptr(cache_seqlens), n, int(max_cache_len), _ptr(result),
+        _stream()))
+    return result

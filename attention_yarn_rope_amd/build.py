@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgptoss_attn.so")
 
-SOURCES = ["api.cpp", "rope.hip", "prefill.hip", "window.hip", "decode.hip", "backward.hip", "kvcache.hip", "projection.hip", "merge.hip"]
+SOURCES = ["api.cpp", "rope.hip", "prefill.hip", "window.hip", "decode.hip", "backward.hip", "kvcache.hip", "projection.hip", "merge.hip", "checks.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -1023,4 +1023,17 @@ gptoss_status gptoss_kv_append(const gptoss_kv_layout* layout, void* k_cache, vo
   return hip_status(launch_kv_append(p, static_cast<hipStream_t>(stream)), "KV append kernel");
 }
 
+gptoss_status gptoss_check_lengths(const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                                   const int32_t* cache_seqlens, int32_t num_seqs, int32_t max_cache_len,
+                                   int32_t* result, void* stream) {
+  if (!result) return fail(GPTOSS_ERR_NULL, "result (3 device int32) is required");
+  if (cu_seqlens && batch < 0) return fail(GPTOSS_ERR_SHAPE, "batch must be >= 0");
+  if (cache_seqlens && (num_seqs < 0 || max_cache_len < 1))
+    return fail(GPTOSS_ERR_SHAPE, "num_seqs must be >= 0 and max_cache_len >= 1");
+  return hip_status(launch_check_lengths(cu_seqlens, cu_seqlens ? batch : 0, total_tokens, cache_seqlens,
+                                         cache_seqlens ? num_seqs : 0, max_cache_len, result,
+                                         static_cast<hipStream_t>(stream)),
+                    "length check kernel");
+}
+
 }  // extern "C"

@@ -186,6 +186,11 @@ struct MergeParams {
   int32_t parts, tokens, num_q_heads;
 };
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+// ---- check of device-resident lengths ----
+hipError_t launch_check_lengths(const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                                const int32_t* cache_seqlens, int32_t num_seqs, int32_t max_cache_len,
+                                int32_t* result, hipStream_t stream);
 constexpr int kProjTile = 256;   // tokens and output features per work group
 
 // ---- KV append ----

@@ -516,6 +516,34 @@ gptoss_status gptoss_qkv_proj_rope(const gptoss_seq_desc* desc, const void* x, i
                                    int32_t table_rows, int32_t rotary_dim, void* q_out, void* k_out,
                                    void* v_out, void* stream);
 
+/*
+ * Check of the device-resident lengths that the attention calls trust (they
+ * clamp every index derived from them, so bad values give wrong results, never
+ * out-of-bounds accesses). For callers and debug runs that want to know: one
+ * small kernel on `stream`, no synchronisation; read `result` once the stream
+ * has reached it.
+ *   cu_seqlens: device int32 [batch + 1] (THD layout) or NULL to skip. Rules:
+ *               cu_seqlens[0] == 0, non-decreasing, and cu_seqlens[batch] ==
+ *               total_tokens when total_tokens >= 0.
+ *   cache_seqlens: device int32 [num_seqs] or NULL to skip. Rule: every length
+ *               in 1 .. max_cache_len (a decode query sits at position L - 1).
+ *   result:     device int32 [3], written by the kernel: result[0] = OR of the
+ *               gptoss_length_fault bits of the broken rules (0: all hold),
+ *               result[1] = the first cu_seqlens index that breaks one (-1 if
+ *               none), result[2] = the first such cache_seqlens index (-1).
+ * Returns GPTOSS_ERR_NULL without result, GPTOSS_ERR_SHAPE for batch < 0 with
+ * cu_seqlens or num_seqs < 0 / max_cache_len < 1 with cache_seqlens.
+ */
+typedef enum {
+  GPTOSS_LEN_CU_START = 1,  /* cu_seqlens[0] != 0 */
+  GPTOSS_LEN_CU_ORDER = 2,  /* cu_seqlens[i] < cu_seqlens[i - 1] for some i */
+  GPTOSS_LEN_CU_TOTAL = 4,  /* cu_seqlens[batch] != total_tokens */
+  GPTOSS_LEN_CACHE = 8      /* a cache length outside 1 .. max_cache_len */
+} gptoss_length_fault;
+gptoss_status gptoss_check_lengths(const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                                   const int32_t* cache_seqlens, int32_t num_seqs, int32_t max_cache_len,
+                                   int32_t* result, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

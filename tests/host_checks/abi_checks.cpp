@@ -165,6 +165,13 @@ int main() {
   EXPECT(gptoss_qkv_proj_rope(&d, P, 2880, 2890, P, P, P, P, P, P, P, 4096, 64, P, P, P, nullptr),
          GPTOSS_ERR_UNSUPPORTED);
 
+  // ---- check of device-resident lengths ----
+  int32_t* const PR = reinterpret_cast<int32_t*>(0x100000);
+  EXPECT(gptoss_check_lengths(PI, 4, 100, PI, 4, 1024, nullptr, nullptr), GPTOSS_ERR_NULL);
+  EXPECT(gptoss_check_lengths(PI, -1, 100, nullptr, 0, 0, PR, nullptr), GPTOSS_ERR_SHAPE);
+  EXPECT(gptoss_check_lengths(nullptr, 0, -1, PI, -2, 1024, PR, nullptr), GPTOSS_ERR_SHAPE);
+  EXPECT(gptoss_check_lengths(nullptr, 0, -1, PI, 4, 0, PR, nullptr), GPTOSS_ERR_SHAPE);
+
   if (failures) std::fprintf(stderr, "%d expectation(s) failed\n", failures);
   else std::printf("all argument checks behaved as documented\n");
   return failures ? 1 : 0;

@@ -29,6 +29,10 @@ hipError_t launch_decode(const DecodeParams&, hipStream_t) { reached("launch_dec
 hipError_t launch_qkv_proj(const ProjParams&, hipStream_t) { reached("launch_qkv_proj"); }
 hipError_t launch_merge(const MergeParams&, hipStream_t) { reached("launch_merge"); }
 hipError_t launch_kv_append(const AppendParams&, hipStream_t) { reached("launch_kv_append"); }
+hipError_t launch_check_lengths(const int32_t*, int32_t, int32_t, const int32_t*, int32_t, int32_t, int32_t*,
+                                hipStream_t) {
+  reached("launch_check_lengths");
+}
 hipError_t static_scratch(void**) { reached("static_scratch"); }
 }  // namespace gptoss
 
