@@ -2,7 +2,8 @@
 
 Also: decode equals the last row of prefill on the same data (the cache holds
 rope_qk's rotated k), results do not depend on the split count beyond fp32
-reassociation, and sequences of length 1 and sinks of -inf behave.
+reassociation, sequences of length 1 and sinks of -inf behave, and 600 sequences
+(several per planning thread) are planned and merged correctly.
 """
 
 import numpy as np
@@ -51,6 +52,15 @@ def test_decode_split_counts(table, splits):
     auto = _run(inp, 0, table)
     assert_close(out, _ref(inp, 0), f"decode splits={splits}")
     assert (np64(out) - np64(auto)).__abs__().max() <= 2 ** -6
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_decode_many_sequences(table, window):
+    """600 sequences (more than the planning kernel's 256 threads, so each thread plans several),
+    cache lengths uniform in [1, 1500], one KV head: every row against the oracle."""
+    inp = wl.decode(600, 1, 1500, seed=25, max_len=1500, hq=8, hkv=1)
+    say(f"[gpu] decode 600 sequences window={window}")
+    assert_close(_run(inp, window, table), _ref(inp, window), f"decode N=600 W={window}")
 
 
 def test_decode_single_split_finish_equals_combine(table):

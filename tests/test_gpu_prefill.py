@@ -101,6 +101,22 @@ def test_thd_ragged(table, window):
     assert_close(out, ref, f"thd W={window}")
 
 
+@pytest.mark.parametrize("window", [0, 128])
+def test_thd_many_short_sequences(table, window):
+    """1500 packed sequences of 0 .. 40 tokens (more sequences than the device scheduler's 1024
+    threads, so each thread walks several; window layers cut them into many short runs), one KV
+    head: every row against the oracle."""
+    g = torch.Generator().manual_seed(520 + window)
+    lengths = torch.randint(0, 41, (1500,), generator=g).tolist()
+    inp = wl.prefill_thd(0, 0, 0, seed=521 + window, lengths=lengths, hq=8, hkv=1)
+    say(f"[gpu] thd 1500 short sequences window={window} (T={sum(lengths)})")
+    out = gx.attn_prefill(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.sinks.cuda(), window=window, table=table,
+                          cu_seqlens=inp.cu_seqlens.cuda(), max_seqlen=inp.max_seqlen)
+    ref = oracle.prefill_thd(np64(inp.q), np64(inp.k), np64(inp.v), inp.cu_seqlens.numpy(), np64(inp.sinks),
+                             TAU, window, CFG)
+    assert_close(out, ref, f"thd N=1500 W={window}")
+
+
 def test_thd_equals_per_sequence_bshd(table):
     lengths = [100, 33, 250]
     inp = wl.prefill_thd(0, 0, 0, seed=12, lengths=lengths)
