@@ -124,6 +124,28 @@ def test_backward_thd(table, window):
     _check((o, lse) + tuple(grads), ref, f"thd W={window}")
 
 
+@pytest.mark.parametrize("window", [0, 128])
+def test_backward_thd_many_short_sequences(table, window):
+    """300 packed sequences of 0 .. 60 tokens, one KV head: the dq and dk / dv work lists hold
+    hundreds of tiny items; every gradient against the oracle."""
+    g = torch.Generator().manual_seed(130 + window)
+    lengths = torch.randint(0, 61, (300,), generator=g).tolist()
+    inp = wl.prefill_thd(0, 0, 0, seed=131 + window, lengths=lengths, hq=8, hkv=1)
+    T = sum(lengths)
+    dout = wl.grad_out((T, 8, 64), 1130 + window)
+    say(f"[gpu] backward thd 300 sequences W={window} (T={T})")
+    q, k, v, s = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.sinks))
+    cu = inp.cu_seqlens.cuda()
+    o, lse = gx.attn_prefill_lse(q, k, v, s, window=window, table=table, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    grads = gx.attn_prefill_backward(q, k, v, s, o, dout.cuda(), lse, window=window, table=table, cu_seqlens=cu,
+                                     max_seqlen=inp.max_seqlen)
+    args = (np64(inp.q), np64(inp.k), np64(inp.v), inp.cu_seqlens.numpy(), np64(inp.sinks), TAU, window,
+            np64(dout), CFG)
+    ref = oracle.prefill_thd_backward(*args)
+    ref["noise"] = bt.noise_thd(*args)
+    _check((o, lse) + tuple(grads), ref, f"thd N=300 W={window}")
+
+
 def test_backward_prerotated_and_deterministic(table):
     """table = None takes q and k as already rotated: gradients then equal the
     rotated-space ones, i.e. R^T undone; two calls give identical bits."""
