@@ -113,6 +113,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * NK * VSB];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
+  static_assert(WAVES == 4 || WAVES == 8, "one wave per query head of the group or of its half");
   constexpr int NTH = 64 * WAVES;
   constexpr int HALVES = kGroup / WAVES;
   const int Hkv = p.num_kv_heads, Hq = Hkv * kGroup;
